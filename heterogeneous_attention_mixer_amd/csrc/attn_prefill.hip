@@ -1,0 +1,411 @@
+// attn_prefill.hip -- flash-style causal prefill of one sequence-mixer layer for gfx950.
+//
+// Variants (Table 1, sec. 3.1 of "Placement Is Free, Composition Is Not: The Latin Square as
+// a Provably-Balanced Construction for Heterogeneous Sequence-Mixer Stacks"):
+//   full          causal softmax attention, scale 1/sqrt(d);
+//   sliding       the same inside a causal window of W keys (query included);
+//   differential  two causal softmax maps over the two halves of the head dimension, scale
+//                 1/sqrt(d/2), combined as (P1 - lambda * P2) V with full-width V.
+//
+// Design (one workgroup = 4 waves = 128 query rows of one (batch, head); 32 rows per wave):
+//   * The scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K is
+//     the A operand (read from LDS), Q the B operand (kept in registers for the whole
+//     kernel). In the 32x32 accumulator a lane owns one query column and 16 key rows, so the
+//     row max and row sum of the softmax are in-lane except for one exchange with lane^32.
+//   * The same accumulator registers, rounded to bf16, are exactly the B operand of
+//     O^T += V^T P^T: P never leaves the registers. V is staged into LDS transposed (V^T,
+//     head-dim rows, key columns) with the key order permuted to match the accumulator
+//     layout, so each A operand is one 16-byte LDS read.
+//   * Online softmax in fp32 with exp2 (the scale is folded with log2(e)); a row whose keys
+//     are all masked so far keeps a finite reference max so no NaN is formed.
+//   * Key tiles of 64 keys; tiles no query of the workgroup can see are never loaded, tiles a
+//     wave cannot see are skipped by that wave, and the element mask is applied only on tiles
+//     that cross the diagonal or the window edge.
+//   * The next tile's K/V is fetched into registers while the current tile is computed.
+//   * Work order: the heaviest query tiles (most visible keys) are dispatched first, and when
+//     the head count allows, all query tiles of a head land on the same XCD (workgroups are
+//     dealt to the 8 XCDs round-robin), so a head's K/V is served from one L2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace mixer {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWave * kWaves;
+constexpr int BM = 128;  // query rows per workgroup
+constexpr int BN = 64;   // keys per tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ------------------------------------------------------------------ small helpers
+
+__device__ __forceinline__ bf16x8 zero8() {
+  bf16x8 z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.0f;
+  return z;
+}
+
+// Eight consecutive elements as bf16 (fp32 sources are rounded to nearest even).
+__device__ __forceinline__ bf16x8 load8(const __bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ bf16x8 load8(const float* p) {
+  floatx4 a = *reinterpret_cast<const floatx4*>(p);
+  floatx4 b = *reinterpret_cast<const floatx4*>(p + 4);
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = (__bf16)a[e];
+    r[e + 4] = (__bf16)b[e];
+  }
+  return r;
+}
+
+// Four consecutive outputs.
+__device__ __forceinline__ void store4(__bf16* p, float a, float b, float c, float d) {
+  bf16x4 r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  r[2] = (__bf16)c;
+  r[3] = (__bf16)d;
+  *reinterpret_cast<bf16x4*>(p) = r;
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  floatx4 r;
+  r[0] = a;
+  r[1] = b;
+  r[2] = c;
+  r[3] = d;
+  *reinterpret_cast<floatx4*>(p) = r;
+}
+
+__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// (batch*head, query tile) of workgroup `bid`: heaviest query tiles first; all tiles of a
+// head on XCD (bid mod 8) when the head count is a multiple of 8.
+__device__ __forceinline__ void map_unit(int bid, int BH, int nq, int* bh, int* qt) {
+  if ((BH & 7) == 0) {
+    const int x = bid & 7, j = bid >> 3, hpx = BH >> 3;
+    *qt = nq - 1 - j / hpx;
+    *bh = x + 8 * (j % hpx);
+  } else {
+    *bh = bid % BH;
+    *qt = nq - 1 - bid / BH;
+  }
+}
+
+// One softmax map of one wave over one key tile. `s` holds the raw scores of the lane's
+// query against its 32 keys of the tile (masked keys = -inf); m is the running max of raw
+// scores, l the lane's partial running sum (the other half of the row lives in lane^32).
+// On return `s` holds the unnormalised probabilities and `alpha` the factor that rescales
+// the previous accumulators.
+__device__ __forceinline__ float softmax_step(floatx16 (&s)[2], float& m, float& l, float c) {
+  float tmax = s[0][0];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  const float m_new = fmaxf(m, tmax);
+  const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
+  const float alpha = fast_exp2((m - m_ref) * c);
+  const float mc = m_ref * c;
+  float psum = 0.0f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -mc));
+      s[kb][r] = p;
+      psum += p;
+    }
+  l = l * alpha + psum;
+  m = m_new;
+  return alpha;
+}
+
+// P (fp32, accumulator layout) -> the four bf16 B operands of the value product.
+__device__ __forceinline__ void pack_p(const floatx16 (&s)[2], bf16x8 (&pf)[2][2]) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[kb][m][e] = (__bf16)s[kb][m * 8 + e];
+}
+
+// ------------------------------------------------------------------ the kernel
+
+template <int D, int VAR, typename Tin>
+__global__ void __launch_bounds__(kThreads)
+prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
+               const Tin* __restrict__ vg, Tin* __restrict__ og, int L, int BH, int nq,
+               int window, float lambda) {
+  constexpr bool kDiff = (VAR == kDifferential);
+  constexpr bool kSlide = (VAR == kSliding);
+  constexpr int KSTEPS = D / 16;          // MFMA steps over the head dim for S^T
+  constexpr int DB = D / 32;              // 32-row blocks of the head dim in O^T
+  constexpr int KP = D + 8;               // K tile row pitch (elements), 16 B pad
+  constexpr int VP = BN + 8;              // V^T tile row pitch (elements), 16 B pad
+  constexpr int KCH = BN * D / 8;         // 16-byte chunks of a K tile
+  constexpr int KPT = KCH / kThreads;     // ... per thread
+  constexpr int VUN = (BN / 4) * (D / 8); // 4-key x 8-channel units of a V tile
+  constexpr int VPT = (VUN + kThreads - 1) / kThreads;
+  static_assert(KCH % kThreads == 0, "K tile staging");
+
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[BN * KP];
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[D * VP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lr = lane & 31;  // query column owned in the accumulators
+  const int lg = lane >> 5;  // lane half
+
+  int bh, qt;
+  map_unit(blockIdx.x, BH, nq, &bh, &qt);
+  const int q0 = qt * BM;
+  const int qw = q0 + wave * 32;  // first query row of this wave
+  const int qi = qw + lr;         // this lane's query row
+  const size_t head = (size_t)bh * (size_t)L * D;
+  const Tin* Q = qg + head;
+  const Tin* K = kg + head;
+  const Tin* V = vg + head;
+  Tin* O = og + head;
+
+  const float c = kLog2e / __builtin_sqrtf(kDiff ? (float)(D / 2) : (float)D);
+
+  // Q fragments (B operand of S^T = K Q^T): lane holds row qi, channels kk*16 + lg*8 + [0,8).
+  bf16x8 qf[KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk)
+    qf[kk] = (qi < L) ? load8(Q + (size_t)qi * D + kk * 16 + lg * 8) : zero8();
+
+  // Key tiles this workgroup can see.
+  const int q_last = min(q0 + BM, L) - 1;
+  int kt_lo = 0;
+  if (kSlide) {
+    const int lo = q0 - window + 1;
+    kt_lo = lo > 0 ? lo / BN : 0;
+  }
+  const int kt_hi = q_last / BN;
+
+  // Accumulators and softmax state (second set only for differential).
+  floatx16 o1[DB], o2[kDiff ? DB : 1];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o1[db][r] = 0.0f;
+  }
+  if constexpr (kDiff) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o2[db][r] = 0.0f;
+  }
+  float m1 = -INFINITY, l1 = 0.0f, m2 = -INFINITY, l2 = 0.0f;
+
+  // Register staging of one K/V tile.
+  bf16x8 kreg[KPT];
+  bf16x8 vreg[VPT][4];
+  auto fetch = [&](int kt) {
+    const int k0 = kt * BN;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int idx = tid + i * kThreads;
+      const int row = idx / (D / 8), ch = idx % (D / 8);
+      const int key = k0 + row;
+      kreg[i] = (key < L) ? load8(K + (size_t)key * D + ch * 8) : zero8();
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int u = tid + i * kThreads;
+      if (u < VUN) {
+        const int a4 = u % (BN / 4), cc = u / (BN / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + a4 * 4 + r;
+          vreg[i][r] = (key < L) ? load8(V + (size_t)key * D + cc * 8) : zero8();
+        }
+      }
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int idx = tid + i * kThreads;
+      const int row = idx / (D / 8), ch = idx % (D / 8);
+      *reinterpret_cast<bf16x8*>(&Ks[row * KP + ch * 8]) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int u = tid + i * kThreads;
+      if (u < VUN) {
+        const int a4 = u % (BN / 4), cc = u / (BN / 4);
+        // Keys 4*a4 .. 4*a4+3 go to column group g16*16 + perm(a4 % 4)*4 of V^T, with
+        // perm = {0, 2, 1, 3}: the order in which the accumulator layout hands out keys.
+        const int grp = a4 & 3;
+        const int col = (a4 >> 2) * 16 + ((grp == 1) ? 2 : (grp == 2) ? 1 : grp) * 4;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          bf16x4 t;
+          t[0] = vreg[i][0][e];
+          t[1] = vreg[i][1][e];
+          t[2] = vreg[i][2][e];
+          t[3] = vreg[i][3][e];
+          *reinterpret_cast<bf16x4*>(&Vt[(cc * 8 + e) * VP + col]) = t;
+        }
+      }
+    }
+  };
+
+  fetch(kt_lo);
+  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+    __syncthreads();  // every wave is done with the previous tile
+    stage();
+    __syncthreads();
+    if (kt < kt_hi) fetch(kt + 1);  // in flight while this tile is computed
+
+    const int k0 = kt * BN;
+    // Does this wave see any key of the tile? (rows qw..qw+31 see keys
+    // [qw - W + 1, qw + 31] together.)
+    bool any = (qw < L) && (k0 <= qw + 31);
+    if (kSlide) any = any && (k0 + BN - 1 >= qw - window + 1);
+    if (!any) continue;
+    // Does every row of the wave see every key of the tile?
+    bool full_tile = (k0 + BN - 1 <= qw);
+    if (kSlide) full_tile = full_tile && (qw + 31 - k0 < window);
+
+    // ---- scores S^T = K Q^T for 64 keys x 32 queries (two 32x32 blocks)
+    floatx16 s1[2], s2[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s1[kb][r] = 0.0f;
+        s2[kb][r] = 0.0f;
+      }
+      const __bf16* krow = &Ks[(kb * 32 + lr) * KP + lg * 8];
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + kk * 16);
+        if (kDiff && kk >= KSTEPS / 2)
+          s2[kb] = mfma32(ka, qf[kk], s2[kb]);
+        else
+          s1[kb] = mfma32(ka, qf[kk], s1[kb]);
+      }
+    }
+
+    // ---- mask on tiles that cross the diagonal or the window edge
+    if (!full_tile) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kj = k0 + kb * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+          bool vis = kj <= qi;
+          if (kSlide) vis = vis && (qi - kj < window);
+          if (!vis) {
+            s1[kb][r] = -INFINITY;
+            if (kDiff) s2[kb][r] = -INFINITY;
+          }
+        }
+    }
+
+    // ---- online softmax, then O^T += V^T P^T
+    bf16x8 p1[2][2], p2[2][2];
+    const float a1 = softmax_step(s1, m1, l1, c);
+    pack_p(s1, p1);
+    float a2 = 1.0f;
+    if constexpr (kDiff) {
+      a2 = softmax_step(s2, m2, l2, c);
+      pack_p(s2, p2);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o1[db][r] *= a1;
+      if constexpr (kDiff) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o2[db][r] *= a2;
+      }
+      const __bf16* vrow = &Vt[(db * 32 + lr) * VP + lg * 8];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(vrow + kb * 32 + m * 16);
+          o1[db] = mfma32(va, p1[kb][m], o1[db]);
+          if constexpr (kDiff) o2[db] = mfma32(va, p2[kb][m], o2[db]);
+        }
+    }
+  }
+
+  // ---- epilogue: out = O / l (differential: O1 / l1 - lambda * O2 / l2). Lanes lane and
+  // lane^32 hold the same query row, so both halves agree on qi < L.
+  const float lsum1 = l1 + __shfl_xor(l1, 32);
+  const float lsum2 = kDiff ? l2 + __shfl_xor(l2, 32) : 1.0f;
+  if (qi < L) {
+    const float inv1 = 1.0f / lsum1;
+    const float inv2 = kDiff ? lambda / lsum2 : 0.0f;
+    Tin* orow = O + (size_t)qi * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = o1[db][r4 * 4 + e] * inv1;
+          if constexpr (kDiff) x[e] -= o2[db][r4 * 4 + e] * inv2;
+        }
+        store4(orow + db * 32 + 8 * r4 + 4 * lg, x[0], x[1], x[2], x[3]);
+      }
+  }
+}
+
+// ------------------------------------------------------------------ launch
+
+template <int D, int VAR, typename Tin>
+static hipError_t launch_t(const PrefillLaunch& a, hipStream_t stream) {
+  const int nq = (a.L + BM - 1) / BM;
+  const int BH = a.B * a.H;
+  const dim3 grid((unsigned)(BH * nq));
+  hipLaunchKernelGGL((prefill_kernel<D, VAR, Tin>), grid, dim3(kThreads), 0, stream,
+                     static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
+                     static_cast<const Tin*>(a.v), static_cast<Tin*>(a.out), a.L, BH, nq,
+                     a.window, a.lambda);
+  return hipGetLastError();
+}
+
+template <int D, typename Tin>
+static hipError_t launch_v(const PrefillLaunch& a, hipStream_t stream) {
+  switch (a.variant) {
+    case kFull: return launch_t<D, kFull, Tin>(a, stream);
+    case kSliding: return launch_t<D, kSliding, Tin>(a, stream);
+    default: return launch_t<D, kDifferential, Tin>(a, stream);
+  }
+}
+
+hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream) {
+  if (a.f32) {
+    return a.d == 64 ? launch_v<64, float>(a, stream) : launch_v<128, float>(a, stream);
+  }
+  return a.d == 64 ? launch_v<64, __bf16>(a, stream) : launch_v<128, __bf16>(a, stream);
+}
+
+int max_grid_units(int L) { return (L + BM - 1) / BM; }
+
+}  // namespace mixer

@@ -1,0 +1,31 @@
+// kernels.h -- internal interface between the host API (mixer_api.cpp) and the gfx950
+// kernels (attn_prefill.hip). Not installed; the public ABI is include/mixer.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace mixer {
+
+enum Variant { kFull = 0, kSliding = 1, kDifferential = 2 };
+
+// One validated layer launch. Pointers are device pointers to [B, H, L, d] tensors of
+// bf16 (f32 == false) or fp32 (f32 == true) elements.
+struct PrefillLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  int variant;
+  int window;
+  float lambda;
+  int B, H, L, d;
+  bool f32;
+};
+
+// Enqueues the layer on `stream`; returns the launch status.
+hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream);
+
+// Query tiles per (batch, head) for a sequence of L tokens.
+int max_grid_units(int L);
+
+}  // namespace mixer

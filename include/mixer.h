@@ -1,0 +1,132 @@
+/*
+ * mixer.h -- C ABI of libmixer.so: causal prefill of one sequence-mixer layer on an MI355X
+ * (gfx950) GPU, in its full, sliding-window and differential variants, plus a Latin-square
+ * layer scheduler.
+ *
+ * Source: "Placement Is Free, Composition Is Not: The Latin Square as a Provably-Balanced
+ * Construction for Heterogeneous Sequence-Mixer Stacks" (arXiv 2609.20269).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are contiguous row-major [B, H, L, d] device pointers (one head's L x d slice
+ *     is contiguous), each starting on a 16-byte boundary. q, k, v and out have the same
+ *     shape; H counts query heads and key/value heads alike (multi-head attention).
+ *   - Ownership: the caller allocates and owns every buffer. The library allocates no device
+ *     memory, keeps no state between calls and never synchronises the device.
+ *   - Asynchrony: the *_async calls and mixer_stack_prefill enqueue work on `stream` (a
+ *     hipStream_t passed as void*, NULL = the legacy default stream) and return. Launch
+ *     errors come back as MIXER_EHIP; a fault during execution surfaces at the caller's next
+ *     synchronisation. Calls on different streams may run from different threads.
+ *   - Validation is host-only and happens before any HIP call: a call that returns an error
+ *     code has not touched the device.
+ *   - Scores are scaled by 1/sqrt(d) (full, sliding) or 1/sqrt(d/2) (differential); there
+ *     is no scale argument.
+ *   - Arithmetic: bf16 operands on the matrix cores with fp32 accumulation; softmax in fp32;
+ *     the probabilities are rounded to bf16 before the value product; outputs are rounded
+ *     once (round-to-nearest-even). Results are bitwise reproducible run to run.
+ */
+#ifndef MIXER_H
+#define MIXER_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Mixer variants, named as in Table 1 (sec. 3.1) of the paper. */
+typedef enum {
+    MIXER_FULL = 0,         /* exact causal attention: key j visible to query i iff j <= i   */
+    MIXER_SLIDING = 1,      /* causal window: visible iff 0 <= i - j <= window - 1            */
+    MIXER_DIFFERENTIAL = 2  /* two half-head-dim maps: out = (P1 - lambda * P2) V             */
+} mixer_variant;
+
+typedef enum {
+    MIXER_OK = 0,
+    MIXER_EINVAL = -1,       /* bad argument: null or unaligned pointer, size < 1, unknown
+                                variant, window < 1 for SLIDING, non-finite lambda for
+                                DIFFERENTIAL, out overlapping q/k/v, size overflow, bad
+                                schedule entry                                             */
+    MIXER_EUNSUPPORTED = -2, /* valid but not built: d not in {64, 128}, grid too large      */
+    MIXER_ENOTLATIN = -3,    /* mixer_stack_prefill: schedule is not a Latin square          */
+    MIXER_EHIP = -4          /* the HIP runtime reported an error at launch                  */
+} mixer_status;
+
+/*
+ * mixer_prefill_async -- one causal-prefill mixer layer, bf16 in and out.
+ *
+ * Defines (Table 1, sec. 3.1; causality as audited in sec. 8), for every b, h and query i:
+ *   FULL          out_i = sum_{j <= i} softmax_j(q_i . k_j / sqrt(d)) v_j
+ *   SLIDING       as FULL over the keys i - window + 1 <= j <= i (the query counts toward
+ *                 the window; window >= L equals FULL; window = 1 returns v)
+ *   DIFFERENTIAL  the head dimension is halved ("halves the head dimension"): q1, k1 are
+ *                 channels [0, d/2), q2, k2 channels [d/2, d); P1, P2 are the causal
+ *                 softmax maps of q1 k1^T / sqrt(d/2) and q2 k2^T / sqrt(d/2); the two maps
+ *                 are subtracted ("subtracts two attention maps"):
+ *                 out_i = sum_{j <= i} (P1_ij - lambda * P2_ij) v_j, v full width d.
+ *
+ * q, k, v   [B, H, L, d] bfloat16 device pointers (read only).
+ * out       [B, H, L, d] bfloat16 device pointer (written); must not overlap q, k or v.
+ * variant   a mixer_variant.
+ * window    SLIDING only, >= 1 (ignored otherwise).
+ * lambda    DIFFERENTIAL only, any finite value (ignored otherwise).
+ * B, H, L   >= 1.   d: 64 or 128.
+ * stream    hipStream_t, or NULL for the legacy default stream.
+ * Returns MIXER_OK or a negative mixer_status.
+ */
+int mixer_prefill_async(const void *q, const void *k, const void *v, void *out,
+                        int variant, int window, float lambda,
+                        int B, int H, int L, int d, void *stream);
+
+/* The same layer on the legacy default stream. */
+int mixer_prefill(const void *q, const void *k, const void *v, void *out,
+                  int variant, int window, float lambda, int B, int H, int L, int d);
+
+/*
+ * mixer_prefill_f32_async -- the same layer for fp32 inputs and output: each element is
+ * rounded to bf16 (nearest-even) as it is loaded, the arithmetic is that of the bf16 entry
+ * point, and the fp32 result is stored without rounding. Same arguments and errors as
+ * mixer_prefill_async, with float pointers.
+ */
+int mixer_prefill_f32_async(const float *q, const float *k, const float *v, float *out,
+                            int variant, int window, float lambda,
+                            int B, int H, int L, int d, void *stream);
+
+/*
+ * mixer_latin_build -- the cyclic Latin square of order N (sec. 1, sec. 3.2; the 4x4
+ * schedule of Table 7 is this construction): sched[r * N + c] = base[(r + c) mod N],
+ * written row-major, so layer l = r * N + c runs type sched[l]. Pure host.
+ * N >= 1; base: N ints; sched: N*N ints (written). Returns MIXER_OK or MIXER_EINVAL.
+ */
+int mixer_latin_build(int N, const int *base, int *sched);
+
+/*
+ * mixer_latin_check -- 1 if the row-major N x N schedule holds exactly N distinct types and
+ * every type appears exactly once in every row and in every column (sec. 1, sec. 3.2),
+ * 0 if not, MIXER_EINVAL for N < 1 or a null pointer. Pure host.
+ */
+int mixer_latin_check(int N, const int *sched);
+
+/*
+ * mixer_stack_prefill -- runs the N*N layers of a Latin-square schedule back to back on one
+ * stream (layer l runs variant sched[l] on q[l], k[l], v[l] into out[l]); the host never
+ * waits between layers.
+ *
+ * sched           N*N mixer_variant values, row-major; must pass mixer_latin_check.
+ * q, k, v, out    host arrays of N*N device pointers, one [B, H, L, d] bf16 tensor each.
+ * window, lambda  used by the SLIDING and DIFFERENTIAL layers respectively.
+ * layer_events    NULL, or a host array of N*N + 1 hipEvent_t (passed as void*): event 0
+ *                 is recorded before layer 0 and event l + 1 after layer l.
+ * Every layer's arguments are validated before the first launch. Returns MIXER_OK,
+ * MIXER_ENOTLATIN (schedule not Latin; nothing launched), or the first layer's error.
+ */
+int mixer_stack_prefill(int N, const int *sched,
+                        const void *const *q, const void *const *k, const void *const *v,
+                        void *const *out, int window, float lambda,
+                        int B, int H, int L, int d, void *stream, void *const *layer_events);
+
+/* A static, human-readable description of a mixer_status (never NULL). */
+const char *mixer_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIXER_H */

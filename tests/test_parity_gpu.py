@@ -1,0 +1,192 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same seeded
+inputs, element by element, with max abs <= 2e-2 and rel-L2 <= 5e-3.
+
+Variants as in Table 1 of "Placement Is Free, Composition Is Not" (full, sliding,
+differential); the causal property is audited as in its sec. 8.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import (assert_close, device_tensors, make, run_layer, sample_rows, to_f64)
+from heterogeneous_attention_mixer_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from heterogeneous_attention_mixer_amd import mixer as M
+    M.lib()
+    return torch
+
+
+def _oracle(oracle_mod, inp, variant, W, lam, rows=None):
+    return oracle_mod.prefill_rows(inp.q, inp.k, inp.v, variant, W, lam, rows)
+
+
+# ------------------------------------------------------------- small, every row compared
+
+def test_fp32_small_full(torch_cuda, oracle_mod):
+    """fp32 inputs, B=1, H=2, L=256, d=64, full causal (rounded to bf16 on load)."""
+    w = synth.WORKLOADS["full_fp32_L256_d64"]
+    inp = make(w["seed"], w["B"], w["H"], w["L"], w["d"], "f32")
+    out = run_layer(device_tensors(inp), "full")
+    assert out.dtype == torch_cuda.float32
+    assert_close(to_f64(out), _oracle(oracle_mod, inp, "full", 0, 0.0), "fp32 L256 d64")
+
+
+SMALL = []
+for d in (64, 128):
+    for L in (1, 2, 63, 64, 128, 129, 777):
+        SMALL.append(("full", d, 2, 3, L, 0, 0.0))
+        SMALL.append(("differential", d, 1, 3, L, 0, 0.8))
+    for L, W in ((777, 1), (777, 37), (777, 64), (777, 100), (777, 128), (777, 777),
+                 (777, 2000), (300, 129), (129, 63)):
+        SMALL.append(("sliding", d, 1, 3, L, W, 0.0))
+    SMALL.append(("differential", d, 2, 2, 300, 0, 0.0))
+    SMALL.append(("differential", d, 1, 2, 300, 0, -0.3))
+
+
+@pytest.mark.parametrize("variant,d,B,H,L,W,lam", SMALL)
+def test_small_every_row(torch_cuda, oracle_mod, variant, d, B, H, L, W, lam):
+    inp = make(1000 + L + d + W, B, H, L, d)
+    out = run_layer(device_tensors(inp), variant, W, lam)
+    assert_close(to_f64(out), _oracle(oracle_mod, inp, variant, W, lam),
+                 f"{variant} d={d} B={B} H={H} L={L} W={W} lam={lam}")
+
+
+@pytest.mark.parametrize("variant,W,lam", [("full", 0, 0.0), ("sliding", 200, 0.0),
+                                           ("differential", 0, 0.8)])
+def test_fp32_every_variant(torch_cuda, oracle_mod, variant, W, lam):
+    inp = make(77, 1, 2, 500, 128, "f32")
+    out = run_layer(device_tensors(inp), variant, W, lam)
+    assert_close(to_f64(out), _oracle(oracle_mod, inp, variant, W, lam), variant)
+
+
+# ------------------------------------------------- full workload sizes, sampled rows
+
+FULLSIZE = [
+    ("sliding_W1024_L8192", 256),
+    ("full_L2048", 256),
+    ("full_L8192", 256),
+    ("differential_L8192", 256),
+    ("full_L32768", 64),
+    ("differential_L32768", 64),
+]
+
+
+@pytest.mark.parametrize("name,n_random", FULLSIZE)
+def test_full_size_sampled_rows(torch_cuda, oracle_mod, name, n_random):
+    w = synth.WORKLOADS[name]
+    inp = make(w["seed"], w["B"], w["H"], w["L"], w["d"])
+    out = run_layer(device_tensors(inp), w["variant"], w["window"], w["lam"])
+    got = out.float()
+    assert bool(torch_cuda.isfinite(got).all()), "non-finite output"
+    rows = sample_rows(w["L"], seed=w["seed"], n_random=n_random)
+    ref = _oracle(oracle_mod, inp, w["variant"], w["window"], w["lam"], rows)
+    assert_close(to_f64(out[:, :, rows]), ref, name)
+
+
+# ------------------------------------------------------------------------ invariants
+
+@pytest.mark.parametrize("variant,W,lam,expect", [("full", 0, 0.0, 1.0),
+                                                  ("sliding", 100, 0.0, 1.0),
+                                                  ("differential", 0, 0.8, 0.2),
+                                                  ("differential", 0, -0.3, 1.3)])
+def test_unit_values_give_row_sums(torch_cuda, variant, W, lam, expect):
+    inp = make(5, 1, 4, 1000, 128)
+    q, k, v = device_tensors(inp)
+    v = torch_cuda.ones_like(v)
+    out = run_layer((q, k, v), variant, W, lam).float()
+    # 4e-3 for the bf16-rounded probabilities, plus half a bf16 ulp for the output rounding
+    assert float((out - expect).abs().max()) <= 4e-3 + abs(expect) * 2.0**-8
+
+
+@pytest.mark.parametrize("L,W", [(777, 777), (777, 5000), (1000, 1000), (128, 128)])
+def test_window_at_least_L_is_full_bitwise(torch_cuda, L, W):
+    t = device_tensors(make(6, 1, 3, L, 128))
+    a = run_layer(t, "sliding", W)
+    b = run_layer(t, "full")
+    assert torch_cuda.equal(a, b)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_window_one_is_v_bitwise(torch_cuda, d):
+    t = device_tensors(make(7, 2, 2, 333, d))
+    assert torch_cuda.equal(run_layer(t, "sliding", 1), t[2])
+
+
+def test_differential_equal_halves(torch_cuda, oracle_mod):
+    """With q1 = q2 and k1 = k2: diff(lambda) = (1 - lambda) diff(0), and diff(0) is plain
+    causal attention on the half-width scores with full-width values."""
+    L, d = 600, 128
+    inp = make(8, 1, 2, L, d)
+    for x in (inp.q, inp.k):
+        x[..., d // 2:] = x[..., :d // 2]
+    for b in (inp.q_bits, inp.k_bits):
+        b[..., d // 2:] = b[..., :d // 2]
+    t = device_tensors(inp)
+    d0 = to_f64(run_layer(t, "differential", 0, 0.0))
+    d8 = to_f64(run_layer(t, "differential", 0, 0.8))
+    assert_close(d8, 0.2 * d0, "diff(0.8) vs 0.2 diff(0)")
+    for h in range(2):
+        ref = oracle_mod.attention_general(inp.q[0, h, :, :d // 2], inp.k[0, h, :, :d // 2],
+                                           inp.v[0, h], 1.0 / np.sqrt(d // 2))
+        assert_close(d0[0, h], ref, f"diff(0) head {h}")
+
+
+# ---------------------------------------------------- causal audit (sec. 8) on the GPU
+
+@pytest.mark.parametrize("variant,W,lam", [("full", 0, 0.0), ("sliding", 70, 0.0),
+                                           ("differential", 0, 0.8)])
+@pytest.mark.parametrize("t", [0, 63, 64, 200, 511])
+def test_future_inputs_do_not_change_past_rows(torch_cuda, variant, W, lam, t):
+    L = 700
+    inp = make(9, 1, 2, L, 128)
+    a = run_layer(device_tensors(inp), variant, W, lam)
+    rng = np.random.default_rng(10 + t)
+    for bits in (inp.q_bits, inp.k_bits, inp.v_bits):
+        bits[:, :, t + 1:] = rng.integers(0, 2**16, size=bits[:, :, t + 1:].shape,
+                                          dtype=np.uint16) & 0x3FFF  # finite, |x| < 2
+    b = run_layer(device_tensors(inp), variant, W, lam)
+    assert torch_cuda.equal(a[:, :, :t + 1], b[:, :, :t + 1])
+    assert not torch_cuda.equal(a[:, :, t + 1:], b[:, :, t + 1:])
+
+
+def test_keys_outside_window_do_not_change_row(torch_cuda):
+    L, W, i = 700, 90, 500
+    inp = make(11, 1, 2, L, 128)
+    a = run_layer(device_tensors(inp), "sliding", W)
+    inp.k_bits[:, :, :i - W + 1] = 0x3F80  # 1.0
+    inp.v_bits[:, :, :i - W + 1] = 0xC000  # -2.0
+    b = run_layer(device_tensors(inp), "sliding", W)
+    assert torch_cuda.equal(a[:, :, i:], b[:, :, i:])  # rows >= i see none of them
+
+
+# ------------------------------------------- determinism, coverage of out, no stray writes
+
+@pytest.mark.parametrize("variant,W,lam", [("full", 0, 0.0), ("sliding", 1024, 0.0),
+                                           ("differential", 0, 0.8)])
+def test_bitwise_reproducible(torch_cuda, variant, W, lam):
+    t = device_tensors(make(12, 1, 16, 4096, 128))
+    a = run_layer(t, variant, W, lam)
+    b = run_layer(t, variant, W, lam)
+    assert torch_cuda.equal(a, b)
+
+
+@pytest.mark.parametrize("L", [1, 127, 129, 1000])
+@pytest.mark.parametrize("variant", ["full", "sliding", "differential"])
+def test_every_row_written_and_nothing_else(torch_cuda, variant, L):
+    import torch
+    B, H, d = 2, 3, 128
+    inp = make(13, B, H, L, d)
+    q, k, v = device_tensors(inp)
+    n = B * H * L * d
+    buf = torch.full((n + 4096,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    buf[n:] = 1024.0
+    out = buf[:n].view(B, H, L, d)
+    run_layer((q, k, v), variant, 50, 0.5, out=out)
+    assert bool(torch.isfinite(out.float()).all())
+    assert bool((buf[n:].float() == 1024.0).all())
