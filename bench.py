@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Benchmark of the mixer hot path on one MI355X.
+
+One step = one pass of the 3x3 Latin-square stack ("Placement Is Free, Composition Is Not",
+sec. 1 and sec. 3.2; Table 3 lists the per-layer prefill cost of each variant at 2K/8K/32K):
+nine causal-prefill layers, rows [full, sliding, differential], [sliding, differential,
+full], [differential, full, sliding], at B=1, H=16 (16 heads of head_dim 128, Table 2),
+L=8192, sliding window 1024, lambda 0.8, each layer with its own seeded bf16 q/k/v already
+resident in HBM. The nine launches go back to back on one stream through
+``mixer_stack_prefill``.
+
+Reported (one JSON line):
+  value           useful attention TFLOP/s of the whole step (4*d flops per visible
+                  query-key pair, summed over the nine layers, / step time);
+  per_variant     per-layer kernel time and useful TFLOP/s of each variant at L=8K, from HIP
+                  events recorded between the launches inside the timed steps, and the
+                  fraction of the dense bf16 MFMA peak;
+  roofline        the same for the kernel that takes most of the step time;
+  cpu_baseline    the fp64 oracle on a bounded row sample of the same layers (host cores).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       [--copy-calibration] [--sweep]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# Dense bf16 MFMA peak of MI355X: 256 CUs x 4 SIMDs x 1024 flop/clk x 2.4 GHz.
+PEAK_BF16_TFLOPS = 2516.6
+HBM_PEAK_GBS = 8000.0
+VARIANT_NAMES = ("full", "sliding", "differential")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "heterogeneous_attention_mixer_amd", "csrc", f)
+                  for f in ("attn_prefill.hip", "kernels.h")]
+
+
+def visible_pairs(variant: str, L: int, window: int) -> int:
+    """Visible (query, key) pairs of one head: causal L(L+1)/2; sliding keeps W per row
+    once the row index reaches W."""
+    if variant == "sliding" and window < L:
+        return window * (window + 1) // 2 + (L - window) * window
+    return L * (L + 1) // 2
+
+
+def useful_flops(variant: str, B: int, H: int, L: int, d: int, window: int) -> int:
+    """4*d flops per visible pair: 2*d for the scores (the differential's two half-width
+    maps together also cost 2*d) and 2*d for the weighted sum of values."""
+    return 4 * d * B * H * visible_pairs(variant, L, window)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(variant: str):
+    """HBM bytes per launch of ``variant`` from the committed counter summary, or None when
+    there is none or the kernel source changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            line = line.strip()
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    key = f"{variant}_hbm_bytes_per_launch"
+    return float(kv[key]) if key in kv else None
+
+
+def cpu_baseline(host_layers, sched, cfg, rows_per_head: int):
+    """The fp64 oracle, as it stands, on a seeded sample of query rows of the first three
+    layers of the stack (one of each variant). Returns the cpu_baseline object."""
+    import numpy as np
+
+    import oracle
+    oracle.build(force=False)
+    rng = np.random.default_rng(12345)
+    L, d, B, H = cfg["L"], cfg["d"], cfg["B"], cfg["H"]
+    flops = 0
+    elapsed = 0.0
+    for layer in range(3):
+        variant = VARIANT_NAMES[sched[layer]]
+        inp = host_layers[layer]
+        q, k, v = (np.ascontiguousarray(x, dtype=np.float64) for x in (inp.q, inp.k, inp.v))
+        rows = np.sort(rng.choice(L, size=rows_per_head, replace=False))
+        t0 = time.perf_counter()
+        oracle.prefill_rows(q, k, v, variant, cfg["window"], cfg["lam"], rows)
+        elapsed += time.perf_counter() - t0
+        for i in rows.tolist():
+            lo = max(0, i - cfg["window"] + 1) if variant == "sliding" else 0
+            flops += 4 * d * B * H * (i - lo + 1)
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": (f"{rows_per_head} seeded query rows per head of layers 0-2 of the stack "
+                   f"(full, sliding W={cfg['window']}, differential lambda={cfg['lam']}), "
+                   f"B={B} H={H} L={L} d={d}, fp64 loops; {flops / 1e9:.1f} GFLOP in "
+                   f"{elapsed:.1f} s"),
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="oracle rows per head per layer for the CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 256 MiB device copy first (for HBM counter scaling)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time full at L=2K/32K and differential at L=32K")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+              "supported (the layer shards over batch and heads with no exchange; see the "
+              "design notes)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from heterogeneous_attention_mixer_amd import build as mbuild
+    from heterogeneous_attention_mixer_amd import mixer, synth
+    if mbuild.needs_build():
+        mbuild.build()
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    mixer.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cfg = dict(synth.LATIN_STACK)
+    B, H, L, d, W, lam = cfg["B"], cfg["H"], cfg["L"], cfg["d"], cfg["window"], cfg["lam"]
+    base = [VARIANT_NAMES.index(x) for x in cfg["base"]]
+    sched = mixer.mixer_latin_build(base)
+    n_layers = len(sched)
+
+    if args.copy_calibration:
+        n = 256 * 1024 * 1024
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # Inputs: layer l drawn from seed seed0 + l, copied to HBM before any timing.
+    host_layers, qs, ks, vs = [], [], [], []
+    for layer in range(n_layers):
+        inp = synth.make_qkv(cfg["seed0"] + layer, B, H, L, d, "bf16")
+        host_layers.append(inp if layer < 3 else None)
+        t = [torch.from_numpy(b).view(torch.bfloat16).to(dev)
+             for b in (inp.q_bits, inp.k_bits, inp.v_bits)]
+        qs.append(t[0])
+        ks.append(t[1])
+        vs.append(t[2])
+    outs = [torch.empty_like(q) for q in qs]
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        mixer.mixer_stack_prefill(3, sched, qs, ks, vs, outs, W, lam, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, each with HIP events around every layer launch.
+    K = args.steps
+    layer_events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_layers + 1)]
+                    for _ in range(K)]
+    for evs in layer_events:
+        for e in evs:
+            e.record()  # creates the events; the library re-records them on the stream
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(K):
+        step(layer_events[i])
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_per_step = start.elapsed_time(end) / K
+
+    total_flops = sum(useful_flops(VARIANT_NAMES[v], B, H, L, d, W) for v in sched)
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+
+    per_launch = {name: [] for name in VARIANT_NAMES}
+    for evs in layer_events:
+        for layer in range(n_layers):
+            per_launch[VARIANT_NAMES[sched[layer]]].append(
+                evs[layer].elapsed_time(evs[layer + 1]))
+    per_variant = {}
+    for name, ts in per_launch.items():
+        if not ts:
+            continue
+        ms = sum(ts) / len(ts)
+        fl = useful_flops(name, B, H, L, d, W)
+        per_variant[name] = {
+            "ms_per_launch": round(ms, 5),
+            "launches": len(ts),
+            "useful_tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+            "frac_of_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "useful_gflop_per_launch": round(fl / 1e9, 3),
+        }
+    dominant = max(per_variant, key=lambda n: per_variant[n]["ms_per_launch"]
+                   * per_variant[n]["launches"])
+    dom = per_variant[dominant]
+    achieved = dom["useful_tflops"]
+    roofline = {
+        "bound": "mfma",
+        "kernel": f"prefill_kernel<128, {dominant}, bf16>",
+        "achieved": achieved,
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": read_traffic(dominant),
+    }
+
+    sweep = None
+    if args.sweep:
+        sweep = {}
+        for name, variant, Ls in (("full", "full", (2048, 32768)),
+                                  ("differential", "differential", (32768,))):
+            for Lx in Ls:
+                inp = synth.make_qkv(3 if variant == "full" else 4, B, H, Lx, d, "bf16")
+                t = [torch.from_numpy(b).view(torch.bfloat16).to(dev)
+                     for b in (inp.q_bits, inp.k_bits, inp.v_bits)]
+                o = torch.empty_like(t[0])
+                for _ in range(3):
+                    mixer.mixer_prefill_async(*t, o, variant, 0, lam)
+                reps = 10 if Lx <= 8192 else 3
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    mixer.mixer_prefill_async(*t, o, variant, 0, lam)
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / reps
+                fl = useful_flops(variant, B, H, Lx, d, 0)
+                sweep[f"{name}_L{Lx}"] = {
+                    "ms_per_launch": round(ms, 5),
+                    "useful_tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                    "frac_of_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                               4)}
+                del t, o
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(host_layers, sched, cfg, args.cpu_rows)
+
+    line = {
+        "metric": "prefill attention TFLOP/s per variant at L=8K; % of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) q/k/v rounded to bf16, fresh per layer",
+        "config": {
+            "workload": (f"3x3 Latin-square stack of causal-prefill layers, rows "
+                         f"[full,sliding,differential],[sliding,differential,full],"
+                         f"[differential,full,sliding]; B={B} H={H} L={L} d={d} "
+                         f"window={W} lambda={lam}"),
+            "B": B, "H": H, "L": L, "d": d, "window": W, "lambda": lam,
+            "layers": n_layers, "useful_gflop_per_step": round(total_flops / 1e9, 2),
+        },
+        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "per_variant": per_variant,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(t_wall, 4),
+    }
+    if sweep is not None:
+        line["sweep"] = sweep
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
