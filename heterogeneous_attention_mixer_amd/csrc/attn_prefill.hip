@@ -7,7 +7,7 @@
 //   differential  two causal softmax maps over the two halves of the head dimension, scale
 //                 1/sqrt(d/2), combined as (P1 - lambda * P2) V with full-width V.
 //
-// Design (one workgroup = 4 waves = 128 query rows of one (batch, head); 32 rows per wave):
+// Design (one workgroup = a few waves of 32 query rows each, all of one (batch, head)):
 //   * The scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K is
 //     the A operand (read from LDS), Q the B operand (kept in registers for the whole
 //     kernel). In the 32x32 accumulator a lane owns one query column and 16 key rows, so the
@@ -16,12 +16,18 @@
 //     O^T += V^T P^T: P never leaves the registers. V is staged into LDS transposed (V^T,
 //     head-dim rows, key columns) with the key order permuted to match the accumulator
 //     layout, so each A operand is one 16-byte LDS read.
-//   * Online softmax in fp32 with exp2 (the scale is folded with log2(e)); a row whose keys
-//     are all masked so far keeps a finite reference max so no NaN is formed.
-//   * Key tiles of 64 keys; tiles no query of the workgroup can see are never loaded, tiles a
-//     wave cannot see are skipped by that wave, and the element mask is applied only on tiles
-//     that cross the diagonal or the window edge.
-//   * The next tile's K/V is fetched into registers while the current tile is computed.
+//   * Online softmax in fp32 with exp2 (the scale is folded with log2(e)). The reference max
+//     of a row is only moved when a new score exceeds it by more than 2^8 in probability
+//     units, so the accumulator rescale (64 multiplies per lane) runs a few times per row
+//     instead of on most tiles; probabilities stay below 256, far from fp32/bf16 limits.
+//     The row sums are taken over the bf16-rounded probabilities (v_dot2 against ones), the
+//     exact weights the value product uses.
+//   * Key tiles of 64 keys, double-buffered in LDS (one barrier per tile); the next tile's
+//     K/V is fetched with buffer loads while the current tile is computed. Each head's
+//     tensors get their own buffer descriptor, so reads past the sequence end return zeros
+//     and need no clamping. Tiles no query of the workgroup can see are never loaded, tiles
+//     a wave cannot see are skipped by that wave, and the element mask is applied only on
+//     tiles that cross the diagonal or the window edge.
 //   * Work order: the heaviest query tiles (most visible keys) are dispatched first, and when
 //     the head count allows, all query tiles of a head land on the same XCD (workgroups are
 //     dealt to the 8 XCDs round-robin), so a head's K/V is served from one L2.
@@ -30,43 +36,70 @@
 
 #include "kernels.h"
 
+#ifndef MIXER_WAVES
+#define MIXER_WAVES 4
+#endif
+
 namespace mixer {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;
-constexpr int kThreads = kWave * kWaves;
-constexpr int BM = 128;  // query rows per workgroup
-constexpr int BN = 64;   // keys per tile
+constexpr int BN = 64;  // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
+// The reference max moves only when a score beats it by more than this many powers of two.
+constexpr float kRescaleLog2Gap = 8.0f;
 
-// ------------------------------------------------------------------ small helpers
+// ------------------------------------------------------------------ buffer access
 
-__device__ __forceinline__ bf16x8 zero8() {
-  bf16x8 z;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.0f;
-  return z;
+// A raw buffer descriptor over `bytes` bytes at `base`; loads at offsets >= bytes return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes,
+                                           0x00020000);
 }
 
-// Eight consecutive elements as bf16 (fp32 sources are rounded to nearest even).
-__device__ __forceinline__ bf16x8 load8(const __bf16* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
+// Eight consecutive elements starting at element `e` as bf16 (fp32 is rounded to nearest
+// even).
+template <typename T>
+__device__ __forceinline__ bf16x8 bload8(__amdgpu_buffer_rsrc_t r, int e);
+template <>
+__device__ __forceinline__ bf16x8 bload8<__bf16>(__amdgpu_buffer_rsrc_t r, int e) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, e * 2, 0, 0));
 }
-__device__ __forceinline__ bf16x8 load8(const float* p) {
-  floatx4 a = *reinterpret_cast<const floatx4*>(p);
-  floatx4 b = *reinterpret_cast<const floatx4*>(p + 4);
-  bf16x8 r;
+template <>
+__device__ __forceinline__ bf16x8 bload8<float>(__amdgpu_buffer_rsrc_t r, int e) {
+  const floatx4 a = __builtin_bit_cast(floatx4,
+                                       __builtin_amdgcn_raw_buffer_load_b128(r, e * 4, 0, 0));
+  const floatx4 b = __builtin_bit_cast(
+      floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, e * 4 + 16, 0, 0));
+  bf16x8 x;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    r[e] = (__bf16)a[e];
-    r[e + 4] = (__bf16)b[e];
+  for (int i = 0; i < 4; ++i) {
+    x[i] = (__bf16)a[i];
+    x[i + 4] = (__bf16)b[i];
   }
-  return r;
+  return x;
+}
+
+// Four consecutive elements.
+template <typename T>
+__device__ __forceinline__ bf16x4 bload4(__amdgpu_buffer_rsrc_t r, int e);
+template <>
+__device__ __forceinline__ bf16x4 bload4<__bf16>(__amdgpu_buffer_rsrc_t r, int e) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, e * 2, 0, 0));
+}
+template <>
+__device__ __forceinline__ bf16x4 bload4<float>(__amdgpu_buffer_rsrc_t r, int e) {
+  const floatx4 a = __builtin_bit_cast(floatx4,
+                                       __builtin_amdgcn_raw_buffer_load_b128(r, e * 4, 0, 0));
+  bf16x4 x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = (__bf16)a[i];
+  return x;
 }
 
 // Four consecutive outputs.
@@ -87,6 +120,8 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
   *reinterpret_cast<floatx4*>(p) = r;
 }
 
+// ------------------------------------------------------------------ math helpers
+
 __device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -106,67 +141,96 @@ __device__ __forceinline__ void map_unit(int bid, int BH, int nq, int* bh, int* 
   }
 }
 
-// One softmax map of one wave over one key tile. `s` holds the raw scores of the lane's
-// query against its 32 keys of the tile (masked keys = -inf); m is the running max of raw
-// scores, l the lane's partial running sum (the other half of the row lives in lane^32).
-// On return `s` holds the unnormalised probabilities and `alpha` the factor that rescales
-// the previous accumulators.
-__device__ __forceinline__ float softmax_step(floatx16 (&s)[2], float& m, float& l, float c) {
+// One softmax map of one wave over one key tile.
+//   s     raw scores of the lane's query against its 32 keys of the tile (masked = -inf);
+//         on return, the probabilities exp2(c * (s - m)) rounded to bf16 are in `pf`;
+//   m     the row's reference max (raw score units), equal in lanes lane and lane^32;
+//   l     the lane's partial row sum (the other half lives in lane^32);
+//   o     the accumulators, rescaled when the reference max moves.
+template <int DB>
+__device__ __forceinline__ void softmax_step(floatx16 (&s)[2], float& m, float& l,
+                                             floatx16 (&o)[DB], bf16x8 (&pf)[2][2], float c,
+                                             float gap) {
   float tmax = s[0][0];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-  const float m_new = fmaxf(m, tmax);
-  const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
-  const float alpha = fast_exp2((m - m_ref) * c);
-  const float mc = m_ref * c;
-  float psum = 0.0f;
+  // Move the reference (and rescale) only if some row of the wave needs it. A row that has
+  // seen no visible key yet has m = -inf and moves as soon as it sees one.
+  if (__any(tmax > m + gap)) {
+    const float m_new = fmaxf(m, tmax);
+    const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2((m - m_new) * c);
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    m = m_new;
+  }
+  const float mc = (m == -INFINITY) ? 0.0f : m * c;
+  bf16x2 ones;
+  ones[0] = (__bf16)1.0f;
+  ones[1] = (__bf16)1.0f;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -mc));
-      s[kb][r] = p;
-      psum += p;
-    }
-  l = l * alpha + psum;
-  m = m_new;
-  return alpha;
-}
-
-// P (fp32, accumulator layout) -> the four bf16 B operands of the value product.
-__device__ __forceinline__ void pack_p(const floatx16 (&s)[2], bf16x8 (&pf)[2][2]) {
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pf[kb][m][e] = (__bf16)s[kb][m * 8 + e];
+      for (int e = 0; e < 8; e += 2) {
+        bf16x2 pp;
+        pp[0] = (__bf16)fast_exp2(__builtin_fmaf(s[kb][h * 8 + e], c, -mc));
+        pp[1] = (__bf16)fast_exp2(__builtin_fmaf(s[kb][h * 8 + e + 1], c, -mc));
+        pf[kb][h][e] = pp[0];
+        pf[kb][h][e + 1] = pp[1];
+        l = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l, false);
+      }
 }
 
 // ------------------------------------------------------------------ the kernel
 
+// Per-variant launch shape. One map (full, sliding): MIXER_WAVES waves of 32 query rows per
+// workgroup, register budget for two waves per SIMD. Two maps (differential): 4 waves and
+// the register budget of one wave per SIMD (it holds two accumulators and two score tiles).
+template <int VAR>
+struct Shape {
+  static constexpr int waves = (VAR == kDifferential) ? 4 : MIXER_WAVES;
+  static constexpr int threads = waves * kWave;
+  static constexpr int bm = 32 * waves;  // query rows per workgroup
+  static constexpr int occupancy = (VAR == kDifferential) ? 1 : 2;
+};
+
 template <int D, int VAR, typename Tin>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __attribute__((amdgpu_flat_work_group_size(Shape<VAR>::threads,
+                                                           Shape<VAR>::threads),
+                               amdgpu_waves_per_eu(Shape<VAR>::occupancy,
+                                                   Shape<VAR>::occupancy)))
 prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
                const Tin* __restrict__ vg, Tin* __restrict__ og, int L, int BH, int nq,
                int window, float lambda) {
   constexpr bool kDiff = (VAR == kDifferential);
   constexpr bool kSlide = (VAR == kSliding);
+  constexpr int kThreads = Shape<VAR>::threads;
+  constexpr int BM = Shape<VAR>::bm;
   constexpr int KSTEPS = D / 16;          // MFMA steps over the head dim for S^T
   constexpr int DB = D / 32;              // 32-row blocks of the head dim in O^T
   constexpr int KP = D + 8;               // K tile row pitch (elements), 16 B pad
   constexpr int VP = BN + 8;              // V^T tile row pitch (elements), 16 B pad
   constexpr int KCH = BN * D / 8;         // 16-byte chunks of a K tile
   constexpr int KPT = KCH / kThreads;     // ... per thread
-  constexpr int VUN = (BN / 4) * (D / 8); // 4-key x 8-channel units of a V tile
+  // V is staged in units of 4 keys x VC channels, transposed in registers: VC = 8 when that
+  // gives every thread a unit, else 4.
+  constexpr int VC = ((BN / 4) * (D / 8) >= kThreads) ? 8 : 4;
+  constexpr int VUN = (BN / 4) * (D / VC);
   constexpr int VPT = (VUN + kThreads - 1) / kThreads;
   static_assert(KCH % kThreads == 0, "K tile staging");
+  typedef __bf16 vcvec __attribute__((ext_vector_type(VC)));
 
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[BN * KP];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[D * VP];
+  // Two K / V^T tile buffers: tile kt is computed from buffer kt & 1 while tile kt + 1 is
+  // written into the other one.
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BN * KP];
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[2][D * VP];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -180,18 +244,19 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
   const int qw = q0 + wave * 32;  // first query row of this wave
   const int qi = qw + lr;         // this lane's query row
   const size_t head = (size_t)bh * (size_t)L * D;
-  const Tin* Q = qg + head;
-  const Tin* K = kg + head;
-  const Tin* V = vg + head;
-  Tin* O = og + head;
+  const int head_bytes = L * D * (int)sizeof(Tin);
+  const __amdgpu_buffer_rsrc_t Qr = make_rsrc(qg + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t Kr = make_rsrc(kg + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t Vr = make_rsrc(vg + head, head_bytes);
 
   const float c = kLog2e / __builtin_sqrtf(kDiff ? (float)(D / 2) : (float)D);
+  const float gap = kRescaleLog2Gap / c;
 
   // Q fragments (B operand of S^T = K Q^T): lane holds row qi, channels kk*16 + lg*8 + [0,8).
+  // Rows past L read zeros and are never stored.
   bf16x8 qf[KSTEPS];
 #pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk)
-    qf[kk] = (qi < L) ? load8(Q + (size_t)qi * D + kk * 16 + lg * 8) : zero8();
+  for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = bload8<Tin>(Qr, qi * D + kk * 16 + lg * 8);
 
   // Key tiles this workgroup can see.
   const int q_last = min(q0 + BM, L) - 1;
@@ -217,65 +282,67 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
   }
   float m1 = -INFINITY, l1 = 0.0f, m2 = -INFINITY, l2 = 0.0f;
 
-  // Register staging of one K/V tile.
+  // Register staging of one K/V tile (element offsets within the head; keys past L read 0).
   bf16x8 kreg[KPT];
-  bf16x8 vreg[VPT][4];
+  vcvec vreg[VPT][4];
   auto fetch = [&](int kt) {
     const int k0 = kt * BN;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int idx = tid + i * kThreads;
       const int row = idx / (D / 8), ch = idx % (D / 8);
-      const int key = k0 + row;
-      kreg[i] = (key < L) ? load8(K + (size_t)key * D + ch * 8) : zero8();
+      kreg[i] = bload8<Tin>(Kr, (k0 + row) * D + ch * 8);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int u = tid + i * kThreads;
-      if (u < VUN) {
+      if (VUN % kThreads == 0 || u < VUN) {
         const int a4 = u % (BN / 4), cc = u / (BN / 4);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int key = k0 + a4 * 4 + r;
-          vreg[i][r] = (key < L) ? load8(V + (size_t)key * D + cc * 8) : zero8();
+          const int off = (k0 + a4 * 4 + r) * D + cc * VC;
+          if constexpr (VC == 8)
+            vreg[i][r] = bload8<Tin>(Vr, off);
+          else
+            vreg[i][r] = bload4<Tin>(Vr, off);
         }
       }
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int idx = tid + i * kThreads;
       const int row = idx / (D / 8), ch = idx % (D / 8);
-      *reinterpret_cast<bf16x8*>(&Ks[row * KP + ch * 8]) = kreg[i];
+      *reinterpret_cast<bf16x8*>(&Ks[buf][row * KP + ch * 8]) = kreg[i];
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int u = tid + i * kThreads;
-      if (u < VUN) {
+      if (VUN % kThreads == 0 || u < VUN) {
         const int a4 = u % (BN / 4), cc = u / (BN / 4);
-        // Keys 4*a4 .. 4*a4+3 go to column group g16*16 + perm(a4 % 4)*4 of V^T, with
+        // Keys 4*a4 .. 4*a4+3 go to column group (a4/4)*16 + perm(a4 % 4)*4 of V^T, with
         // perm = {0, 2, 1, 3}: the order in which the accumulator layout hands out keys.
         const int grp = a4 & 3;
         const int col = (a4 >> 2) * 16 + ((grp == 1) ? 2 : (grp == 2) ? 1 : grp) * 4;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < VC; ++e) {
           bf16x4 t;
           t[0] = vreg[i][0][e];
           t[1] = vreg[i][1][e];
           t[2] = vreg[i][2][e];
           t[3] = vreg[i][3][e];
-          *reinterpret_cast<bf16x4*>(&Vt[(cc * 8 + e) * VP + col]) = t;
+          *reinterpret_cast<bf16x4*>(&Vt[buf][(cc * VC + e) * VP + col]) = t;
         }
       }
     }
   };
 
   fetch(kt_lo);
+  stage(kt_lo & 1);
+  __syncthreads();
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    __syncthreads();  // every wave is done with the previous tile
-    stage();
-    __syncthreads();
+    const int buf = kt & 1;
     if (kt < kt_hi) fetch(kt + 1);  // in flight while this tile is computed
 
     const int k0 = kt * BN;
@@ -283,74 +350,66 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
     // [qw - W + 1, qw + 31] together.)
     bool any = (qw < L) && (k0 <= qw + 31);
     if (kSlide) any = any && (k0 + BN - 1 >= qw - window + 1);
-    if (!any) continue;
-    // Does every row of the wave see every key of the tile?
-    bool full_tile = (k0 + BN - 1 <= qw);
-    if (kSlide) full_tile = full_tile && (qw + 31 - k0 < window);
+    if (any) {
+      // Does every row of the wave see every key of the tile?
+      bool full_tile = (k0 + BN - 1 <= qw);
+      if (kSlide) full_tile = full_tile && (qw + 31 - k0 < window);
 
-    // ---- scores S^T = K Q^T for 64 keys x 32 queries (two 32x32 blocks)
-    floatx16 s1[2], s2[2];
+      // ---- scores S^T = K Q^T for 64 keys x 32 queries (two 32x32 blocks)
+      floatx16 s1[2], s2[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s1[kb][r] = 0.0f;
-        s2[kb][r] = 0.0f;
-      }
-      const __bf16* krow = &Ks[(kb * 32 + lr) * KP + lg * 8];
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + kk * 16);
-        if (kDiff && kk >= KSTEPS / 2)
-          s2[kb] = mfma32(ka, qf[kk], s2[kb]);
-        else
-          s1[kb] = mfma32(ka, qf[kk], s1[kb]);
-      }
-    }
-
-    // ---- mask on tiles that cross the diagonal or the window edge
-    if (!full_tile) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kj = k0 + kb * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
-          bool vis = kj <= qi;
-          if (kSlide) vis = vis && (qi - kj < window);
-          if (!vis) {
-            s1[kb][r] = -INFINITY;
-            if (kDiff) s2[kb][r] = -INFINITY;
-          }
+          s1[kb][r] = 0.0f;
+          s2[kb][r] = 0.0f;
         }
-    }
-
-    // ---- online softmax, then O^T += V^T P^T
-    bf16x8 p1[2][2], p2[2][2];
-    const float a1 = softmax_step(s1, m1, l1, c);
-    pack_p(s1, p1);
-    float a2 = 1.0f;
-    if constexpr (kDiff) {
-      a2 = softmax_step(s2, m2, l2, c);
-      pack_p(s2, p2);
-    }
+        const __bf16* krow = &Ks[buf][(kb * 32 + lr) * KP + lg * 8];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o1[db][r] *= a1;
-      if constexpr (kDiff) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o2[db][r] *= a2;
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + kk * 16);
+          if (kDiff && kk >= KSTEPS / 2)
+            s2[kb] = mfma32(ka, qf[kk], s2[kb]);
+          else
+            s1[kb] = mfma32(ka, qf[kk], s1[kb]);
+        }
       }
-      const __bf16* vrow = &Vt[(db * 32 + lr) * VP + lg * 8];
+
+      // ---- mask on tiles that cross the diagonal or the window edge
+      if (!full_tile) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(vrow + kb * 32 + m * 16);
-          o1[db] = mfma32(va, p1[kb][m], o1[db]);
-          if constexpr (kDiff) o2[db] = mfma32(va, p2[kb][m], o2[db]);
-        }
+          for (int r = 0; r < 16; ++r) {
+            const int kj = k0 + kb * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+            bool vis = kj <= qi;
+            if (kSlide) vis = vis && (qi - kj < window);
+            if (!vis) {
+              s1[kb][r] = -INFINITY;
+              if (kDiff) s2[kb][r] = -INFINITY;
+            }
+          }
+      }
+
+      // ---- online softmax, then O^T += V^T P^T
+      bf16x8 p1[2][2], p2[2][2];
+      softmax_step<DB>(s1, m1, l1, o1, p1, c, gap);
+      if constexpr (kDiff) softmax_step<DB>(s2, m2, l2, o2, p2, c, gap);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const __bf16* vrow = &Vt[buf][(db * 32 + lr) * VP + lg * 8];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const bf16x8 va = *reinterpret_cast<const bf16x8*>(vrow + kb * 32 + h * 16);
+            o1[db] = mfma32(va, p1[kb][h], o1[db]);
+            if constexpr (kDiff) o2[db] = mfma32(va, p2[kb][h], o2[db]);
+          }
+      }
     }
+    if (kt < kt_hi) stage(buf ^ 1);  // that buffer was released by the previous barrier
+    __syncthreads();
   }
 
   // ---- epilogue: out = O / l (differential: O1 / l1 - lambda * O2 / l2). Lanes lane and
@@ -360,7 +419,7 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
   if (qi < L) {
     const float inv1 = 1.0f / lsum1;
     const float inv2 = kDiff ? lambda / lsum2 : 0.0f;
-    Tin* orow = O + (size_t)qi * D;
+    Tin* orow = og + head + (size_t)qi * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -380,10 +439,11 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
 
 template <int D, int VAR, typename Tin>
 static hipError_t launch_t(const PrefillLaunch& a, hipStream_t stream) {
+  constexpr int BM = Shape<VAR>::bm;
   const int nq = (a.L + BM - 1) / BM;
   const int BH = a.B * a.H;
   const dim3 grid((unsigned)(BH * nq));
-  hipLaunchKernelGGL((prefill_kernel<D, VAR, Tin>), grid, dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((prefill_kernel<D, VAR, Tin>), grid, dim3(Shape<VAR>::threads), 0, stream,
                      static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
                      static_cast<const Tin*>(a.v), static_cast<Tin*>(a.out), a.L, BH, nq,
                      a.window, a.lambda);
@@ -406,6 +466,6 @@ hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream) {
   return a.d == 64 ? launch_v<64, __bf16>(a, stream) : launch_v<128, __bf16>(a, stream);
 }
 
-int max_grid_units(int L) { return (L + BM - 1) / BM; }
+int max_grid_units(int L) { return (L + 127) / 128; }  // the smallest bm of any variant
 
 }  // namespace mixer

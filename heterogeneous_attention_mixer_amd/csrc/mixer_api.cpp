@@ -38,6 +38,8 @@ int validate(const void* q, const void* k, const void* v, void* o, int variant, 
   const size_t esz = f32 ? 4 : 2;
   if (elems * esz >= ((unsigned __int128)1 << 62)) return MIXER_EINVAL;
   if (d != 64 && d != 128) return MIXER_EUNSUPPORTED;
+  // One head's L x d slice is addressed with 32-bit byte offsets.
+  if ((unsigned __int128)L * d * esz >= ((unsigned __int128)1 << 31)) return MIXER_EUNSUPPORTED;
   // One workgroup of 256 threads per (batch, head, query tile): the grid must fit in 32 bits
   // of threads.
   const unsigned __int128 wgs = (unsigned __int128)B * H * mixer::max_grid_units(L);

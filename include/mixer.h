@@ -44,7 +44,8 @@ typedef enum {
                                 variant, window < 1 for SLIDING, non-finite lambda for
                                 DIFFERENTIAL, out overlapping q/k/v, size overflow, bad
                                 schedule entry                                             */
-    MIXER_EUNSUPPORTED = -2, /* valid but not built: d not in {64, 128}, grid too large      */
+    MIXER_EUNSUPPORTED = -2, /* valid but not built: d not in {64, 128}, one head's L x d
+                                slice of 2 GiB or more, grid too large                     */
     MIXER_ENOTLATIN = -3,    /* mixer_stack_prefill: schedule is not a Latin square          */
     MIXER_EHIP = -4          /* the HIP runtime reported an error at launch                  */
 } mixer_status;

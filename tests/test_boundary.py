@@ -71,6 +71,7 @@ BAD = [
     (dict(o=P[2] + 64), M.EINVAL),                  # out overlaps v
     (dict(B=2**20, H=2**20, L=2**20, d=128), M.EINVAL),  # byte size overflows
     (dict(B=4096, H=4096, L=65536, d=64), M.EUNSUPPORTED),   # grid too large
+    (dict(B=1, H=1, L=2**23, d=128), M.EUNSUPPORTED),        # one head slice = 2 GiB (bf16)
 ]
 
 
