@@ -16,7 +16,7 @@ Reported (one JSON line):
                   events recorded between the launches inside the timed steps, and the
                   fraction of the dense bf16 MFMA peak;
   roofline        the same for the kernel that takes most of the step time;
-  cpu_baseline    the fp64 oracle on a bounded row sample of the same layers (host cores).
+  cpu_baseline    the fp64 oracle on the same nine layers, every row (host cores).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        [--copy-calibration] [--sweep]
@@ -84,8 +84,9 @@ def read_traffic(variant: str):
 
 
 def cpu_baseline(host_layers, sched, cfg, rows_per_head: int):
-    """The fp64 oracle, as it stands, on a seeded sample of query rows of the first three
-    layers of the stack (one of each variant). Returns the cpu_baseline object."""
+    """The fp64 oracle, as it stands, on the layers of one step (every layer of the stack;
+    every query row, or a seeded sample of ``rows_per_head`` rows per head when that is
+    positive). Returns the cpu_baseline object."""
     import numpy as np
 
     import oracle
@@ -94,23 +95,26 @@ def cpu_baseline(host_layers, sched, cfg, rows_per_head: int):
     L, d, B, H = cfg["L"], cfg["d"], cfg["B"], cfg["H"]
     flops = 0
     elapsed = 0.0
-    for layer in range(3):
+    for layer, inp in enumerate(host_layers):
         variant = VARIANT_NAMES[sched[layer]]
-        inp = host_layers[layer]
-        q, k, v = (np.ascontiguousarray(x, dtype=np.float64) for x in (inp.q, inp.k, inp.v))
-        rows = np.sort(rng.choice(L, size=rows_per_head, replace=False))
+        if 0 < rows_per_head < L:
+            rows = np.sort(rng.choice(L, size=rows_per_head, replace=False))
+        else:
+            rows = None
         t0 = time.perf_counter()
-        oracle.prefill_rows(q, k, v, variant, cfg["window"], cfg["lam"], rows)
+        oracle.prefill_rows(inp.q, inp.k, inp.v, variant, cfg["window"], cfg["lam"], rows)
         elapsed += time.perf_counter() - t0
-        for i in rows.tolist():
+        for i in (range(L) if rows is None else rows.tolist()):
             lo = max(0, i - cfg["window"] + 1) if variant == "sliding" else 0
             flops += 4 * d * B * H * (i - lo + 1)
+    what = ("every query row" if not 0 < rows_per_head < L
+            else f"{rows_per_head} seeded query rows per head")
     return {
         "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.max_threads(),
         "kind": "oracle",
-        "sample": (f"{rows_per_head} seeded query rows per head of layers 0-2 of the stack "
+        "sample": (f"{what} of all {len(host_layers)} layers of one step of the stack "
                    f"(full, sliding W={cfg['window']}, differential lambda={cfg['lam']}), "
                    f"B={B} H={H} L={L} d={d}, fp64 loops; {flops / 1e9:.1f} GFLOP in "
                    f"{elapsed:.1f} s"),
@@ -123,8 +127,8 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=4096,
-                    help="oracle rows per head per layer for the CPU baseline")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="oracle rows per head per layer for the CPU baseline (0 = all)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB device copy first (for HBM counter scaling)")
     ap.add_argument("--sweep", action="store_true",
@@ -169,7 +173,7 @@ def main(argv=None) -> int:
     host_layers, qs, ks, vs = [], [], [], []
     for layer in range(n_layers):
         inp = synth.make_qkv(cfg["seed0"] + layer, B, H, L, d, "bf16")
-        host_layers.append(inp if layer < 3 else None)
+        host_layers.append(inp)
         t = [torch.from_numpy(b).view(torch.bfloat16).to(dev)
              for b in (inp.q_bits, inp.k_bits, inp.v_bits)]
         qs.append(t[0])
