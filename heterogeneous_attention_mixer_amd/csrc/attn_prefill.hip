@@ -7,7 +7,7 @@
 //   differential  two causal softmax maps over the two halves of the head dimension, scale
 //                 1/sqrt(d/2), combined as (P1 - lambda * P2) V with full-width V.
 //
-// Design (one workgroup = a few waves of 32 query rows each, all of one (batch, head)):
+// Design (one workgroup = one (batch, head) and a block of query rows, 32 rows per wave):
 //   * The scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K is
 //     the A operand (read from LDS), Q the B operand (kept in registers for the whole
 //     kernel). In the 32x32 accumulator a lane owns one query column and 16 key rows, so the
@@ -22,6 +22,10 @@
 //     instead of on most tiles; probabilities stay below 256, far from fp32/bf16 limits.
 //     The row sums are taken over the bf16-rounded probabilities (v_dot2 against ones), the
 //     exact weights the value product uses.
+//   * The differential variant gives each of its two softmax maps its own wave: the two
+//     waves of a row block read the same K/V tiles (scores on their half of the head dim,
+//     values on all of it) and meet once, at the end, through LDS. Each wave then carries
+//     one accumulator set, so it fits the register budget of two waves per SIMD.
 //   * Key tiles of 64 keys, double-buffered in LDS (one barrier per tile); the next tile's
 //     K/V is fetched with buffer loads while the current tile is computed. Each head's
 //     tensors get their own buffer descriptor, so reads past the sequence end return zeros
@@ -34,10 +38,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 #ifndef MIXER_WAVES
 #define MIXER_WAVES 4
+#endif
+#ifndef MIXER_DIFF_ROWS
+#define MIXER_DIFF_ROWS 4
 #endif
 
 namespace mixer {
@@ -53,6 +62,8 @@ constexpr int BN = 64;  // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 // The reference max moves only when a score beats it by more than this many powers of two.
 constexpr float kRescaleLog2Gap = 8.0f;
+// s_waitcnt immediate (gfx9 encoding): vmcnt = 0, expcnt and lgkmcnt left at their maxima.
+constexpr int kWaitVm0 = 0x0F70;
 
 // ------------------------------------------------------------------ buffer access
 
@@ -190,15 +201,20 @@ __device__ __forceinline__ void softmax_step(floatx16 (&s)[2], float& m, float& 
 
 // ------------------------------------------------------------------ the kernel
 
-// Per-variant launch shape. One map (full, sliding): MIXER_WAVES waves of 32 query rows per
-// workgroup, register budget for two waves per SIMD. Two maps (differential): 4 waves and
-// the register budget of one wave per SIMD (it holds two accumulators and two score tiles).
+// Per-variant launch shape. A workgroup covers `rows` blocks of 32 query rows of one
+// (batch, head). Full and sliding: one wave per row block. Differential: two waves per row
+// block, one per softmax map (map 0 on head-dim channels [0, d/2), map 1 on [d/2, d)); both
+// stream the same K/V tiles from LDS and combine their outputs through LDS at the end, so
+// each wave holds one accumulator set, like a full-attention wave with half-width scores.
+// Register budget: two waves per SIMD.
 template <int VAR>
 struct Shape {
-  static constexpr int waves = (VAR == kDifferential) ? 4 : MIXER_WAVES;
+  static constexpr int maps = (VAR == kDifferential) ? 2 : 1;
+  static constexpr int rows = (VAR == kDifferential) ? MIXER_DIFF_ROWS : MIXER_WAVES;
+  static constexpr int waves = rows * maps;
   static constexpr int threads = waves * kWave;
-  static constexpr int bm = 32 * waves;  // query rows per workgroup
-  static constexpr int occupancy = (VAR == kDifferential) ? 1 : 2;
+  static constexpr int bm = 32 * rows;  // query rows per workgroup
+  static constexpr int occupancy = 2;
 };
 
 template <int D, int VAR, typename Tin>
@@ -212,8 +228,10 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
   constexpr bool kDiff = (VAR == kDifferential);
   constexpr bool kSlide = (VAR == kSliding);
   constexpr int kThreads = Shape<VAR>::threads;
+  constexpr int kRows = Shape<VAR>::rows;
   constexpr int BM = Shape<VAR>::bm;
-  constexpr int KSTEPS = D / 16;          // MFMA steps over the head dim for S^T
+  constexpr int KSTEPS = D / 16;          // MFMA steps over the head dim
+  constexpr int NQ = KSTEPS / Shape<VAR>::maps;  // ... over one map's score channels
   constexpr int DB = D / 32;              // 32-row blocks of the head dim in O^T
   constexpr int KP = D + 8;               // K tile row pitch (elements), 16 B pad
   constexpr int VP = BN + 8;              // V^T tile row pitch (elements), 16 B pad
@@ -227,21 +245,29 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
   static_assert(KCH % kThreads == 0, "K tile staging");
   typedef __bf16 vcvec __attribute__((ext_vector_type(VC)));
 
-  // Two K / V^T tile buffers: tile kt is computed from buffer kt & 1 while tile kt + 1 is
-  // written into the other one.
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BN * KP];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[2][D * VP];
+  // LDS: two K / V^T tile buffers (tile kt is computed from buffer kt & 1 while tile kt + 1
+  // is written into the other one); after the key loop the differential reuses the space
+  // to pass map 1's scaled output to map 0.
+  constexpr int kKsElems = BN * KP, kVtElems = D * VP;
+  constexpr int kTileBytes = 2 * (kKsElems + kVtElems) * 2;
+  constexpr int kXchBytes = kDiff ? kRows * 64 * (DB * 16) * 4 : 0;
+  constexpr int kSmemBytes = kTileBytes > kXchBytes ? kTileBytes : kXchBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  __bf16* const Ks0 = reinterpret_cast<__bf16*>(smem);
+  __bf16* const Vt0 = Ks0 + 2 * kKsElems;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int rb = wave % kRows;            // row block of this wave
+  const int map = wave / kRows;           // softmax map of this wave (differential)
   const int lr = lane & 31;  // query column owned in the accumulators
   const int lg = lane >> 5;  // lane half
 
   int bh, qt;
   map_unit(blockIdx.x, BH, nq, &bh, &qt);
   const int q0 = qt * BM;
-  const int qw = q0 + wave * 32;  // first query row of this wave
+  const int qw = q0 + rb * 32;    // first query row of this wave
   const int qi = qw + lr;         // this lane's query row
   const size_t head = (size_t)bh * (size_t)L * D;
   const int head_bytes = L * D * (int)sizeof(Tin);
@@ -251,12 +277,18 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
 
   const float c = kLog2e / __builtin_sqrtf(kDiff ? (float)(D / 2) : (float)D);
   const float gap = kRescaleLog2Gap / c;
+  // First score channel of this wave's map.
+  const int ch0 = kDiff ? map * (D / 2) : 0;
 
-  // Q fragments (B operand of S^T = K Q^T): lane holds row qi, channels kk*16 + lg*8 + [0,8).
-  // Rows past L read zeros and are never stored.
-  bf16x8 qf[KSTEPS];
+  // Q fragments (B operand of S^T = K Q^T): lane holds row qi, channels
+  // ch0 + kk*16 + lg*8 + [0,8). Rows past L read zeros and are never stored.
+  bf16x8 qf[NQ];
 #pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = bload8<Tin>(Qr, qi * D + kk * 16 + lg * 8);
+  for (int kk = 0; kk < NQ; ++kk) qf[kk] = bload8<Tin>(Qr, qi * D + ch0 + kk * 16 + lg * 8);
+  // Wait for Q here, once: otherwise the wait-count insertion cannot prove inside the key
+  // loop that Q has arrived, and makes every tile's first score products wait for all
+  // vector loads in flight, the next tile's prefetch included.
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
   // Key tiles this workgroup can see.
   const int q_last = min(q0 + BM, L) - 1;
@@ -267,20 +299,14 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
   }
   const int kt_hi = q_last / BN;
 
-  // Accumulators and softmax state (second set only for differential).
-  floatx16 o1[DB], o2[kDiff ? DB : 1];
+  // Accumulators and softmax state of this wave's map.
+  floatx16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o1[db][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   }
-  if constexpr (kDiff) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o2[db][r] = 0.0f;
-  }
-  float m1 = -INFINITY, l1 = 0.0f, m2 = -INFINITY, l2 = 0.0f;
+  float m = -INFINITY, l = 0.0f;
 
   // Register staging of one K/V tile (element offsets within the head; keys past L read 0).
   bf16x8 kreg[KPT];
@@ -310,11 +336,13 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
     }
   };
   auto stage = [&](int buf) {
+    __bf16* const Ks = Ks0 + buf * kKsElems;
+    __bf16* const Vt = Vt0 + buf * kVtElems;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int idx = tid + i * kThreads;
       const int row = idx / (D / 8), ch = idx % (D / 8);
-      *reinterpret_cast<bf16x8*>(&Ks[buf][row * KP + ch * 8]) = kreg[i];
+      *reinterpret_cast<bf16x8*>(&Ks[row * KP + ch * 8]) = kreg[i];
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -332,7 +360,7 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
           t[1] = vreg[i][1][e];
           t[2] = vreg[i][2][e];
           t[3] = vreg[i][3][e];
-          *reinterpret_cast<bf16x4*>(&Vt[buf][(cc * VC + e) * VP + col]) = t;
+          *reinterpret_cast<bf16x4*>(&Vt[(cc * VC + e) * VP + col]) = t;
         }
       }
     }
@@ -354,27 +382,21 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
       // Does every row of the wave see every key of the tile?
       bool full_tile = (k0 + BN - 1 <= qw);
       if (kSlide) full_tile = full_tile && (qw + 31 - k0 < window);
+      const __bf16* const Ks = Ks0 + buf * kKsElems;
+      const __bf16* const Vt = Vt0 + buf * kVtElems;
 
-      // ---- scores S^T = K Q^T for 64 keys x 32 queries (two 32x32 blocks)
-      floatx16 s1[2], s2[2];
+      // ---- scores S^T = K Q^T for 64 keys x 32 queries (two 32x32 blocks) over this
+      // wave's score channels
+      floatx16 s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s1[kb][r] = 0.0f;
-          s2[kb][r] = 0.0f;
-        }
-        const __bf16* krow = &Ks[buf][(kb * 32 + lr) * KP + lg * 8];
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+        const __bf16* krow = &Ks[(kb * 32 + lr) * KP + ch0 + lg * 8];
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + kk * 16);
-          if (kDiff && kk >= KSTEPS / 2)
-            s2[kb] = mfma32(ka, qf[kk], s2[kb]);
-          else
-            s1[kb] = mfma32(ka, qf[kk], s1[kb]);
-        }
+        for (int kk = 0; kk < NQ; ++kk)
+          s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(krow + kk * 16), qf[kk], s[kb]);
       }
-
       // ---- mask on tiles that cross the diagonal or the window edge
       if (!full_tile) {
 #pragma unroll
@@ -384,41 +406,47 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
             const int kj = k0 + kb * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
             bool vis = kj <= qi;
             if (kSlide) vis = vis && (qi - kj < window);
-            if (!vis) {
-              s1[kb][r] = -INFINITY;
-              if (kDiff) s2[kb][r] = -INFINITY;
-            }
+            if (!vis) s[kb][r] = -INFINITY;
           }
       }
-
       // ---- online softmax, then O^T += V^T P^T
-      bf16x8 p1[2][2], p2[2][2];
-      softmax_step<DB>(s1, m1, l1, o1, p1, c, gap);
-      if constexpr (kDiff) softmax_step<DB>(s2, m2, l2, o2, p2, c, gap);
+      bf16x8 p[2][2];
+      softmax_step<DB>(s, m, l, o, p, c, gap);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const __bf16* vrow = &Vt[buf][(db * 32 + lr) * VP + lg * 8];
+        const __bf16* vrow = &Vt[(db * 32 + lr) * VP + lg * 8];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const bf16x8 va = *reinterpret_cast<const bf16x8*>(vrow + kb * 32 + h * 16);
-            o1[db] = mfma32(va, p1[kb][h], o1[db]);
-            if constexpr (kDiff) o2[db] = mfma32(va, p2[kb][h], o2[db]);
-          }
+          for (int h = 0; h < 2; ++h)
+            o[db] = mfma32(*reinterpret_cast<const bf16x8*>(vrow + kb * 32 + h * 16),
+                           p[kb][h], o[db]);
       }
     }
     if (kt < kt_hi) stage(buf ^ 1);  // that buffer was released by the previous barrier
     __syncthreads();
   }
 
-  // ---- epilogue: out = O / l (differential: O1 / l1 - lambda * O2 / l2). Lanes lane and
-  // lane^32 hold the same query row, so both halves agree on qi < L.
-  const float lsum1 = l1 + __shfl_xor(l1, 32);
-  const float lsum2 = kDiff ? l2 + __shfl_xor(l2, 32) : 1.0f;
+  // ---- epilogue: out = O / l; differential: out = O1 / l1 - lambda * O2 / l2, with map 1's
+  // term passed to map 0 through LDS (the key loop ended with a barrier, so the tile buffers
+  // are free). Lanes lane and lane^32 hold the same query row. Element (db, r) of a lane is
+  // head-dim channel db*32 + 8*(r/4) + 4*lg + r%4 of query qi.
+  const float lsum = l + __shfl_xor(l, 32);
+  if constexpr (kDiff) {
+    float* const xch = reinterpret_cast<float*>(smem) + rb * 64 * (DB * 16);
+    if (map == 1) {
+      const float sc = lambda / lsum;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xch[(db * 16 + r) * 64 + lane] = o[db][r] * sc;
+    }
+    __syncthreads();
+    if (map == 1) return;
+  }
   if (qi < L) {
-    const float inv1 = 1.0f / lsum1;
-    const float inv2 = kDiff ? lambda / lsum2 : 0.0f;
+    const float inv = 1.0f / lsum;
+    const float* const xch = reinterpret_cast<const float*>(smem) + rb * 64 * (DB * 16);
     Tin* orow = og + head + (size_t)qi * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -427,8 +455,8 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
         float x[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          x[e] = o1[db][r4 * 4 + e] * inv1;
-          if constexpr (kDiff) x[e] -= o2[db][r4 * 4 + e] * inv2;
+          x[e] = o[db][r4 * 4 + e] * inv;
+          if constexpr (kDiff) x[e] -= xch[(db * 16 + r4 * 4 + e) * 64 + lane];
         }
         store4(orow + db * 32 + 8 * r4 + 4 * lg, x[0], x[1], x[2], x[3]);
       }
@@ -466,6 +494,6 @@ hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream) {
   return a.d == 64 ? launch_v<64, __bf16>(a, stream) : launch_v<128, __bf16>(a, stream);
 }
 
-int max_grid_units(int L) { return (L + 127) / 128; }  // the smallest bm of any variant
+int max_grid_units(int L) { return (L + 31) / 32; }  // bm >= 32 for every variant
 
 }  // namespace mixer
