@@ -83,6 +83,57 @@ def read_traffic(variant: str):
     return float(kv[key]) if key in kv else None
 
 
+COPY_BYTES = 256 * 1024 * 1024  # the --copy-calibration copy: reads and writes this much
+KERNEL_VARIANT_TAGS = {"ILi128ELi0E": "full", "ILi128ELi1E": "sliding",
+                       "ILi128ELi2E": "differential"}
+
+
+def write_traffic(fetch_csv: str, write_csv: str, command: str) -> str:
+    """Turn two rocprofv3 --pmc counter files (FETCH_SIZE, then WRITE_SIZE, in KiB per
+    dispatch, of ``bench.py --copy-calibration``) into HBM bytes per launch of each d=128
+    bf16 variant. Each counter is scaled so that the plain device copy of COPY_BYTES reads
+    (or writes) exactly COPY_BYTES. Writes TRAFFIC_FILE, keyed to the kernel source hash."""
+    import csv
+
+    def per_kernel(path, counter):
+        out = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"]
+                key = next((v for k, v in KERNEL_VARIANT_TAGS.items()
+                            if "prefill_kernel" in name and k in name and "DF16b" in name),
+                           "copy" if "copyBuffer" in name else None)
+                if key:
+                    out.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
+        return {k: sum(v) / len(v) for k, v in out.items()}
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    if "copy" not in fetch or "copy" not in write:
+        raise SystemExit("no copy-kernel calibration in the counter files")
+    fscale = COPY_BYTES / fetch["copy"]
+    wscale = COPY_BYTES / write["copy"]
+    lines = ["# HBM bytes per launch of prefill_kernel<128, variant, bf16> at B=1 H=16 L=8192",
+             "# (Latin stack workload), from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE,",
+             "# each scaled by what it reads for a plain 256 MiB device copy.",
+             f"# command: {command}",
+             f"kernel_source_sha256_16 = {kernel_source_hash()}",
+             f"fetch_scale = {fscale:.4f}",
+             f"write_scale = {wscale:.4f}"]
+    for v in VARIANT_NAMES:
+        if v in fetch and v in write:
+            lines.append(f"{v}_fetch_bytes_per_launch = {fetch[v] * fscale:.0f}")
+            lines.append(f"{v}_write_bytes_per_launch = {write[v] * wscale:.0f}")
+            lines.append(f"{v}_hbm_bytes_per_launch = "
+                         f"{fetch[v] * fscale + write[v] * wscale:.0f}")
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return TRAFFIC_FILE
+
+
 def cpu_baseline(host_layers, sched, cfg, rows_per_head: int):
     """The fp64 oracle, as it stands, on the layers of one step (every layer of the stack;
     every query row, or a seeded sample of ``rows_per_head`` rows per head when that is
@@ -133,7 +184,17 @@ def main(argv=None) -> int:
                     help="run a plain 256 MiB device copy first (for HBM counter scaling)")
     ap.add_argument("--sweep", action="store_true",
                     help="also time full at L=2K/32K and differential at L=32K")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="host only: write the HBM traffic summary from two rocprofv3 "
+                         "counter files and exit")
+    ap.add_argument("--traffic-command", default="",
+                    help="with --write-traffic: the profiling command, recorded in the file")
     args = ap.parse_args(argv)
+
+    if args.write_traffic:
+        print(write_traffic(args.write_traffic[0], args.write_traffic[1],
+                            args.traffic_command))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
