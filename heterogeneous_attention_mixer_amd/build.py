@@ -12,8 +12,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmixer.so")
-SOURCES = [os.path.join(CSRC, "attn_prefill.hip"), os.path.join(CSRC, "mixer_api.cpp")]
-HEADERS = [os.path.join(CSRC, "kernels.h"), os.path.join(ROOT, "include", "mixer.h")]
+SOURCES = [os.path.join(CSRC, f)
+           for f in ("attn_prefill.hip", "attn_prefill_dma.hip", "mixer_api.cpp")]
+HEADERS = [os.path.join(CSRC, f) for f in ("kernels.h", "device_common.h")] + [
+    os.path.join(ROOT, "include", "mixer.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

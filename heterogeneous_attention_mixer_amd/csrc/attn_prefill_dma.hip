@@ -1,0 +1,481 @@
+// attn_prefill_dma.hip -- bf16 causal prefill of one sequence-mixer layer for gfx950, with
+// K/V tiles moved HBM -> LDS by the buffer unit (no register staging) and a software
+// pipeline that overlaps each tile's softmax with the matrix products of its neighbours.
+//
+// Variants (Table 1, sec. 3.1 of "Placement Is Free, Composition Is Not: The Latin Square as
+// a Provably-Balanced Construction for Heterogeneous Sequence-Mixer Stacks"):
+//   full          causal softmax attention, scale 1/sqrt(d);
+//   sliding       the same inside a causal window of W keys (query included);
+//   differential  two causal softmax maps over the two halves of the head dimension, scale
+//                 1/sqrt(d/2), combined as (P1 - lambda * P2) V with full-width V.
+//
+// Design (one workgroup = one (batch, head) and a block of query rows, 32 rows per wave):
+//   * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16 (K from LDS
+//     as the A operand, Q held in registers as the B operand). A lane owns one query column
+//     and 16 keys of each 32-key block, so row max and row sum are in-lane plus one
+//     permlane32 swap with lane^32.
+//   * Those accumulators, rounded to bf16, are the B operand of O^T += V^T P^T. The V^T
+//     operand is read from the row-major V tile with ds_read_b64_tr_b16: a 16-lane group
+//     reading 4 key rows x 16 channels receives, per lane, one channel across the 4 keys.
+//     The keys are taken in the order the score accumulator hands them out, so P never
+//     moves between lanes.
+//   * K and V tiles (64 keys) are written into LDS by buffer loads with the LDS flag: each
+//     wave instruction moves 1 KiB (64 lanes x 16 B) straight from HBM, with no VGPRs and no
+//     VALU work; keys past the end of the sequence are outside the head's buffer range and
+//     arrive as zeros. Each 256 B (d=128) row is stored with its 16 B chunks permuted by an
+//     XOR of the row index, which keeps both the K reads (16 rows, one chunk each) and the
+//     transposed V reads (4 rows, 4 chunks each per 32 lanes) free of bank conflicts.
+//   * Pipeline: K runs two tiles ahead of V. Iteration j issues the loads of K[j+2] and V[j],
+//     then computes O += V[j-1] P[j-1] together with the row max of S[j], and the
+//     exponentials of S[j] together with S[j+1] = K[j+1] Q^T; the matrix core and the vector
+//     ALU work on independent data in each half. Two K and two V buffers, one barrier per
+//     tile.
+//   * Online softmax in fp32 with exp2 (scale folded with log2 e); the reference max moves
+//     only when a score beats it by more than 2^8 (probabilities stay below 256), so the
+//     accumulator rescale is rare. Row sums are taken over the bf16-rounded probabilities,
+//     the exact weights of the value product.
+//   * The differential gives each softmax map its own wave (scores on its half of the head
+//     dim, values on all of it); the two waves of a row block meet once, at the end,
+//     through LDS.
+//   * Work order: heaviest query tiles first; all tiles of a head on one XCD when B*H is a
+//     multiple of 8.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "kernels.h"
+
+#ifndef MIXER_WAVES
+#define MIXER_WAVES 4
+#endif
+#ifndef MIXER_DIFF_ROWS
+#define MIXER_DIFF_ROWS 4
+#endif
+
+namespace mixer {
+
+namespace dma {
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Launch shape: `rows` blocks of 32 query rows per workgroup; the differential adds a
+// second wave per row block for its second map. Register budget: two waves per SIMD.
+template <int VAR>
+struct DShape {
+  static constexpr int maps = (VAR == kDifferential) ? 2 : 1;
+  static constexpr int rows = (VAR == kDifferential) ? MIXER_DIFF_ROWS : MIXER_WAVES;
+  static constexpr int waves = rows * maps;
+  static constexpr int threads = waves * kWave;
+  static constexpr int bm = 32 * rows;
+};
+
+// Chunk swizzle of a tile row: the 16-byte chunk c of row r is stored at chunk c ^ swz(r).
+// d = 128 (16 chunks per 256 B row): swaps the two 2-bit halves of r mod 16, a bijection
+// on any 16 aligned rows, and gives 4 consecutive rows 4 different 4-chunk groups.
+// d = 64 (8 chunks per 128 B row, two rows per bank sweep): the same two properties for
+// rows of equal parity.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128)
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  else
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// 16 bytes per lane from buffer offset `voff` of `r` into LDS at dst + 16 * lane (dst is
+// wave-uniform); offsets outside the buffer's range write zeros. The builtin is compiled in
+// the device pass only: seen by the host pass inside a kernel template, it makes that pass
+// drop the kernel's launch stub.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, lds_char* dst, int voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+#endif
+}
+
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
+}
+
+// Value of lane ^ 32 next to the lane's own: returns (own, other) combined by `op`.
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __builtin_fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+template <int D, int VAR>
+__global__ void __attribute__((amdgpu_flat_work_group_size(DShape<VAR>::threads,
+                                                           DShape<VAR>::threads),
+                               amdgpu_waves_per_eu(2, 2)))
+prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
+                   const __bf16* __restrict__ vg, __bf16* __restrict__ og, int L, int BH,
+                   int nq, int window, float lambda) {
+  constexpr bool kDiff = (VAR == kDifferential);
+  constexpr bool kSlide = (VAR == kSliding);
+  constexpr int kWaves = DShape<VAR>::waves;
+  constexpr int kRows = DShape<VAR>::rows;
+  constexpr int BM = DShape<VAR>::bm;
+  constexpr int KSTEPS = D / 16;                  // MFMA steps over the head dim
+  constexpr int NQ = KSTEPS / DShape<VAR>::maps;  // ... over one map's score channels
+  constexpr int DB = D / 32;                      // 32-channel blocks of O^T
+  constexpr int ROWB = D * 2;                     // bytes per K/V row
+  constexpr int TILEB = BN * ROWB;                // bytes per K/V tile
+  constexpr int NI = TILEB / 1024;                // 1 KiB load instructions per tile
+  constexpr int NIW = NI / kWaves;                // ... per wave
+  constexpr int CPR = D / 8;                      // 16-byte chunks per row
+  static_assert(NI % kWaves == 0, "tile loads must split evenly over the waves");
+
+  // LDS: K buffers 0, 1 then V buffers 0, 1; reused after the key loop by the differential.
+  constexpr int kXchBytes = kDiff ? kRows * 64 * (DB * 16) * 4 : 0;
+  constexpr int kSmem = (4 * TILEB > kXchBytes) ? 4 * TILEB : kXchBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
+  lds_char* const lds = (lds_char*)(smem);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rb = wave % kRows;  // row block of this wave
+  const int map = wave / kRows;  // softmax map of this wave (differential)
+  const int lr = lane & 31;
+  const int lg = lane >> 5;
+
+  int bh, qt;
+  map_unit(blockIdx.x, BH, nq, &bh, &qt);
+  const int q0 = qt * BM;
+  const int qw = q0 + rb * 32;
+  const int qi = qw + lr;
+  const size_t head = (size_t)bh * (size_t)L * D;
+  const int head_bytes = L * ROWB;
+  const __amdgpu_buffer_rsrc_t Qr = make_rsrc(qg + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t Kr = make_rsrc(kg + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t Vr = make_rsrc(vg + head, head_bytes);
+
+  const float c = kLog2e / __builtin_sqrtf(kDiff ? (float)(D / 2) : (float)D);
+  const float gap = kRescaleLog2Gap / c;
+  const int ch0 = kDiff ? map * (D / 2) : 0;  // first score channel of this wave's map
+
+  // Q fragments: lane holds row qi, channels ch0 + kk*16 + lg*8 + [0, 8).
+  bf16x8 qf[NQ];
+#pragma unroll
+  for (int kk = 0; kk < NQ; ++kk) qf[kk] = bload8<__bf16>(Qr, qi * D + ch0 + kk * 16 + lg * 8);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+
+  // ---- per-lane address parts, fixed for the whole kernel
+  // Tile loads: instruction i of this wave covers rows [R0, R0 + 1024/ROWB) of the tile;
+  // lane `lane` fills chunk slot lane % CPR of row R0 + lane / CPR, i.e. logical chunk
+  // (lane % CPR) ^ swz(row).
+  int ld_off[NIW];
+#pragma unroll
+  for (int t = 0; t < NIW; ++t) {
+    const int i = wave + t * kWaves;
+    const int r = i * (1024 / ROWB) + lane / CPR;
+    ld_off[t] = r * ROWB + (((lane % CPR) ^ swz<D>(r)) << 4);
+  }
+  // K operand reads: row kb*32 + lr (the swizzle depends on the row mod 16 only), chunk
+  // ch0/8 + 2*kk + lg.
+  const int k_sw = swz<D>(lr);
+  int k_off[NQ];
+#pragma unroll
+  for (int kk = 0; kk < NQ; ++kk)
+    k_off[kk] = lr * ROWB + (((ch0 / 8 + 2 * kk + lg) ^ k_sw) << 4);
+  // V^T operand reads (transposed, 8 bytes per lane): for the 16-key half h of key block kb
+  // and read rr, lane (group g = lane/16, s = lane%16) reads key row
+  // kb*32 + 16h + 8rr + 4*lg + s/4, channels db*32 + 16*(g%2) + 4*(s%4) + [0, 4).
+  const int vs = lane & 15, vdh = (lane >> 4) & 1;
+  int v_off[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int r = 8 * rr + 4 * lg + (vs >> 2);
+      const int chunk = 4 * db + 2 * vdh + ((vs & 3) >> 1);
+      v_off[db][rr] = r * ROWB + ((chunk ^ swz<D>(r)) << 4) + (vs & 1) * 8;
+    }
+
+  // ---- key tiles the workgroup can see: [lo, hi]
+  const int q_last = min(q0 + BM, L) - 1;
+  const int lo = kSlide ? max(0, q0 - window + 1) / BN : 0;
+  const int hi = q_last / BN;
+
+  // LDS byte offsets of the K and V buffers holding tile j.
+  auto k_buf = [&](int j) { return (j & 1) * TILEB; };
+  auto v_buf = [&](int j) { return 2 * TILEB + (j & 1) * TILEB; };
+  // Tile j of K (v = false) or V (v = true) into the LDS buffer at byte offset `dst`.
+  auto load_tile = [&](bool v, int dst, int j) {
+    const int base = j * TILEB;
+#pragma unroll
+    for (int t = 0; t < NIW; ++t)
+      lds_load16(v ? Vr : Kr, lds + dst + (wave + t * kWaves) * 1024, base + ld_off[t]);
+  };
+  // Does every row of the wave see every key of tile j?
+  auto full_tile = [&](int j) {
+    const int k0 = j * BN;
+    bool f = (k0 + BN - 1 <= qw);
+    if (kSlide) f = f && (qw + 31 - k0 < window);
+    return f;
+  };
+
+  floatx16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+  float m = -INFINITY, l = 0.0f;
+  floatx16 s[2];      // scores of the tile being worked on
+  bf16x8 pp[2][2];    // probabilities of the previous tile (value product pending)
+
+  // S^T = K[j] Q^T over this wave's score channels, into `d`.
+  auto qk_into = [&](int j, floatx16(&d)[2]) {
+    const lds_char* kb_ = lds + k_buf(j);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) d[kb][r] = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < NQ; ++kk) {
+        const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+            kb_ + kb * 32 * ROWB + k_off[kk]);
+        d[kb] = mfma32(a, qf[kk], d[kb]);
+      }
+    }
+  };
+  auto qk = [&](int j) { qk_into(j, s); };
+  // O^T += V[j]^T P^T.
+  auto pv = [&](int j, const bf16x8 (&p)[2][2]) {
+    lds_char* vb = lds + v_buf(j);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int roff = (kb * 32 + 16 * h) * ROWB;
+          const shortx4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              reinterpret_cast<__attribute__((address_space(3))) shortx4*>(
+                  vb + roff + v_off[db][0]));
+          const shortx4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              reinterpret_cast<__attribute__((address_space(3))) shortx4*>(
+                  vb + roff + v_off[db][1]));
+          // One whole-vector shuffle and one bit cast: assembling the operand element by
+          // element (bf16 from 16-bit integers) was lowered to a wrong byte permutation.
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[db] = mfma32(a, p[kb][h], o[db]);
+        }
+  };
+  auto mask = [&](int j) {
+    const int k0 = j * BN;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kj = k0 + kb * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+        bool vis = kj <= qi;
+        if (kSlide) vis = vis && (qi - kj < window);
+        if (!vis) s[kb][r] = -INFINITY;
+      }
+  };
+  auto row_max = [&]() {
+    float t0 = max3(s[0][0], s[0][1], s[0][2]);
+    float t1 = max3(s[1][0], s[1][1], s[1][2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) {
+      t0 = max3(t0, s[0][r], s[0][r + 1]);
+      t1 = max3(t1, s[1][r], s[1][r + 1]);
+    }
+    t0 = max3(t0, s[0][15], t1);
+    t0 = __builtin_fmaxf(t0, s[1][15]);
+    return xhalf_max(t0);
+  };
+  // Probabilities exp2(c (s - m)) rounded to bf16 into `p`; their sum added to l.
+  auto exps = [&](bf16x8 (&p)[2][2]) {
+    const float mc = (m == -INFINITY) ? 0.0f : m * c;
+    bf16x2 ones;
+    ones[0] = (__bf16)1.0f;
+    ones[1] = (__bf16)1.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          bf16x2 q2;
+          q2[0] = (__bf16)fast_exp2(__builtin_fmaf(s[kb][h * 8 + e], c, -mc));
+          q2[1] = (__bf16)fast_exp2(__builtin_fmaf(s[kb][h * 8 + e + 1], c, -mc));
+          p[kb][h][e] = q2[0];
+          p[kb][h][e + 1] = q2[1];
+          l = __builtin_amdgcn_fdot2_f32_bf16(q2, ones, l, false);
+        }
+  };
+
+  // ---- prologue: zero both V buffers (the first iteration multiplies P = 0 by the buffer
+  // of tile lo-1, which must hold finite values); K[lo], K[lo+1] into LDS; S = K[lo] Q^T.
+  {
+    const floatx4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+    floatx4* const vz = reinterpret_cast<floatx4*>(smem + 2 * TILEB);
+#pragma unroll
+    for (int i = tid; i < 2 * TILEB / 16; i += kWaves * kWave) vz[i] = z;
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pp[kb][h][e] = (__bf16)0.0f;
+  load_tile(false, k_buf(lo), lo);
+  if (lo + 1 <= hi) load_tile(false, k_buf(lo + 1), lo + 1);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  qk(lo);
+  __syncthreads();
+
+  // ---- key loop. Every wave runs the same sequence on every tile of the workgroup's
+  // range: keys a wave cannot see are masked (probability 0, softmax state unchanged), so
+  // the loop body is one straight path and the register allocation stays within two waves
+  // per SIMD.
+  float alpha_p = 1.0f;   // pending rescale of O, decided on the previous tile
+  bool moved_p = false;
+  for (int j = lo; j <= hi; ++j) {
+    // Loads for the next iteration: K[j+2] into K's buffer j & 1 (K[j] was read during
+    // iteration j-1) and V[j] into V's buffer j & 1 (V[j-2] was read during j-1).
+    if (j + 2 <= hi) load_tile(false, k_buf(j), j + 2);
+    load_tile(true, v_buf(j), j);
+
+    // Rescale decided on tile j-1: O holds tiles up to j-2 here, and the value product of
+    // tile j-1 below is already on tile j-1's reference.
+    if (moved_p) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha_p;
+    }
+    if (!full_tile(j)) mask(j);
+    // Reference move for tile j (rare): m and l follow at once, O at the next iteration.
+    const float tmax = row_max();
+    float alpha = 1.0f;
+    const bool moved = __any(tmax > m + gap);
+    if (moved) {
+      const float m_new = __builtin_fmaxf(m, tmax);
+      alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2((m - m_new) * c);
+      l *= alpha;
+      m = m_new;
+    }
+    // One straight block: O += V[j-1] P[j-1], the exponentials of tile j and
+    // S[j+1] = K[j+1] Q^T (on the last tile it reads a stale buffer and is discarded).
+    // The group barriers fix the issue order so that vector work sits between the matrix
+    // instructions: a wave issues in order, and an MFMA waiting for the busy matrix pipe
+    // holds up everything behind it.
+    bf16x8 pn[2][2];
+    floatx16 sn[2];
+    pv(j - 1, pp);
+    exps(pn);
+    qk_into(j + 1, sn);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
+    constexpr int kMfma = DB * 4 + 2 * NQ;  // matrix instructions in the block
+    constexpr int kValu = 96 / kMfma + 1;   // vector instructions between two of them
+#pragma unroll
+    for (int i = 0; i < kMfma / 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);      // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = sn[kb];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) pp[kb][h] = pn[kb][h];
+    }
+    alpha_p = alpha;
+    moved_p = moved;
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+  }
+  if (moved_p) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha_p;
+  }
+  pv(hi, pp);
+
+  // ---- epilogue: out = O / l; differential: O1 / l1 - lambda * O2 / l2 with map 1's term
+  // passed to map 0 through LDS. Element (db, r) of a lane is channel
+  // db*32 + 8*(r/4) + 4*lg + r%4 of query qi.
+  const float lsum = xhalf_sum(l);
+  if constexpr (kDiff) {
+    __syncthreads();  // every wave is done reading the V tiles
+    float* const xch = reinterpret_cast<float*>(smem) + rb * 64 * (DB * 16);
+    if (map == 1) {
+      const float sc = lambda / lsum;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xch[(db * 16 + r) * 64 + lane] = o[db][r] * sc;
+    }
+    __syncthreads();
+    if (map == 1) return;
+  }
+  if (qi < L) {
+    const float inv = 1.0f / lsum;
+    const float* const xch = reinterpret_cast<const float*>(smem) + rb * 64 * (DB * 16);
+    __bf16* orow = og + head + (size_t)qi * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = o[db][r4 * 4 + e] * inv;
+          if constexpr (kDiff) x[e] -= xch[(db * 16 + r4 * 4 + e) * 64 + lane];
+        }
+        store4(orow + db * 32 + 8 * r4 + 4 * lg, x[0], x[1], x[2], x[3]);
+      }
+  }
+}
+
+template <int D, int VAR>
+hipError_t launch_dma_t(const PrefillLaunch& a, hipStream_t stream) {
+  constexpr int BM = DShape<VAR>::bm;
+  const int nq = (a.L + BM - 1) / BM;
+  const int BH = a.B * a.H;
+  hipLaunchKernelGGL((prefill_dma_kernel<D, VAR>), dim3((unsigned)(BH * nq)),
+                     dim3(DShape<VAR>::threads), 0, stream, static_cast<const __bf16*>(a.q),
+                     static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
+                     static_cast<__bf16*>(a.out), a.L, BH, nq, a.window, a.lambda);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dma_v(const PrefillLaunch& a, hipStream_t stream) {
+  switch (a.variant) {
+    case kFull: return launch_dma_t<D, kFull>(a, stream);
+    case kSliding: return launch_dma_t<D, kSliding>(a, stream);
+    default: return launch_dma_t<D, kDifferential>(a, stream);
+  }
+}
+
+}  // namespace dma
+
+hipError_t launch_prefill_dma(const PrefillLaunch& a, hipStream_t stream) {
+  return a.d == 64 ? dma::launch_dma_v<64>(a, stream) : dma::launch_dma_v<128>(a, stream);
+}
+
+hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream) {
+#ifdef MIXER_BF16_REGSTAGE
+  return launch_prefill_regstage(a, stream);
+#else
+  return a.f32 ? launch_prefill_regstage(a, stream) : launch_prefill_dma(a, stream);
+#endif
+}
+
+}  // namespace mixer

@@ -1,0 +1,110 @@
+// device_common.h -- device-side helpers shared by the prefill kernels (gfx950): vector
+// types, buffer-descriptor loads, MFMA and exp2 wrappers, the work order of the grid.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace mixer {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int BN = 64;  // keys per tile
+constexpr float kLog2e = 1.4426950408889634f;
+// The reference max moves only when a score beats it by more than this many powers of two.
+constexpr float kRescaleLog2Gap = 8.0f;
+// s_waitcnt immediate (gfx9 encoding): vmcnt = 0, expcnt and lgkmcnt left at their maxima.
+constexpr int kWaitVm0 = 0x0F70;
+
+// ------------------------------------------------------------------ buffer access
+
+// A raw buffer descriptor over `bytes` bytes at `base`; loads at offsets >= bytes return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes,
+                                           0x00020000);
+}
+
+// Eight consecutive elements starting at element `e` as bf16 (fp32 is rounded to nearest
+// even).
+template <typename T>
+__device__ __forceinline__ bf16x8 bload8(__amdgpu_buffer_rsrc_t r, int e);
+template <>
+__device__ __forceinline__ bf16x8 bload8<__bf16>(__amdgpu_buffer_rsrc_t r, int e) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, e * 2, 0, 0));
+}
+template <>
+__device__ __forceinline__ bf16x8 bload8<float>(__amdgpu_buffer_rsrc_t r, int e) {
+  const floatx4 a = __builtin_bit_cast(floatx4,
+                                       __builtin_amdgcn_raw_buffer_load_b128(r, e * 4, 0, 0));
+  const floatx4 b = __builtin_bit_cast(
+      floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, e * 4 + 16, 0, 0));
+  bf16x8 x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = (__bf16)a[i];
+    x[i + 4] = (__bf16)b[i];
+  }
+  return x;
+}
+
+// Four consecutive elements.
+template <typename T>
+__device__ __forceinline__ bf16x4 bload4(__amdgpu_buffer_rsrc_t r, int e);
+template <>
+__device__ __forceinline__ bf16x4 bload4<__bf16>(__amdgpu_buffer_rsrc_t r, int e) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, e * 2, 0, 0));
+}
+template <>
+__device__ __forceinline__ bf16x4 bload4<float>(__amdgpu_buffer_rsrc_t r, int e) {
+  const floatx4 a = __builtin_bit_cast(floatx4,
+                                       __builtin_amdgcn_raw_buffer_load_b128(r, e * 4, 0, 0));
+  bf16x4 x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = (__bf16)a[i];
+  return x;
+}
+
+// Four consecutive outputs.
+__device__ __forceinline__ void store4(__bf16* p, float a, float b, float c, float d) {
+  bf16x4 r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  r[2] = (__bf16)c;
+  r[3] = (__bf16)d;
+  *reinterpret_cast<bf16x4*>(p) = r;
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  floatx4 r;
+  r[0] = a;
+  r[1] = b;
+  r[2] = c;
+  r[3] = d;
+  *reinterpret_cast<floatx4*>(p) = r;
+}
+
+// ------------------------------------------------------------------ math helpers
+
+__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// (batch*head, query tile) of workgroup `bid`: heaviest query tiles first; all tiles of a
+// head on XCD (bid mod 8) when the head count is a multiple of 8.
+__device__ __forceinline__ void map_unit(int bid, int BH, int nq, int* bh, int* qt) {
+  if ((BH & 7) == 0) {
+    const int x = bid & 7, j = bid >> 3, hpx = BH >> 3;
+    *qt = nq - 1 - j / hpx;
+    *bh = x + 8 * (j % hpx);
+  } else {
+    *bh = bid % BH;
+    *qt = nq - 1 - bid / BH;
+  }
+}
+
+}  // namespace mixer

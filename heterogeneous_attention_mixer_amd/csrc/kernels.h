@@ -22,8 +22,12 @@ struct PrefillLaunch {
   bool f32;
 };
 
-// Enqueues the layer on `stream`; returns the launch status.
+// Enqueues the layer on `stream`; returns the launch status. bf16 layers run the LDS-DMA
+// kernel (attn_prefill_dma.hip), fp32 layers the register-staged kernel (attn_prefill.hip),
+// which rounds to bf16 as it stages.
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream);
+hipError_t launch_prefill_dma(const PrefillLaunch& a, hipStream_t stream);
+hipError_t launch_prefill_regstage(const PrefillLaunch& a, hipStream_t stream);
 
 // Query tiles per (batch, head) for a sequence of L tokens.
 int max_grid_units(int L);
