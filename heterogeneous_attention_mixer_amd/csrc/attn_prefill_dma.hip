@@ -42,6 +42,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -93,8 +95,12 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, lds_char* d
 #endif
 }
 
-__device__ __forceinline__ float max3(float a, float b, float c) {
-  return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
+// max(a, b, c) in one v_max3_f32. The operands are finite or -inf (scores, masked scores),
+// never NaN, so the input canonicalization that fmaxf implies is not needed.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 // Value of lane ^ 32 next to the lane's own: returns (own, other) combined by `op`.
@@ -140,6 +146,7 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // the same value, in an SGPR
   const int rb = wave % kRows;  // row block of this wave
   const int map = wave / kRows;  // softmax map of this wave (differential)
   const int lr = lane & 31;
@@ -204,14 +211,12 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   const int hi = q_last / BN;
 
   // LDS byte offsets of the K and V buffers holding tile j.
-  auto k_buf = [&](int j) { return (j & 1) * TILEB; };
-  auto v_buf = [&](int j) { return 2 * TILEB + (j & 1) * TILEB; };
   // Tile j of K (v = false) or V (v = true) into the LDS buffer at byte offset `dst`.
   auto load_tile = [&](bool v, int dst, int j) {
     const int base = j * TILEB;
 #pragma unroll
     for (int t = 0; t < NIW; ++t)
-      lds_load16(v ? Vr : Kr, lds + dst + (wave + t * kWaves) * 1024, base + ld_off[t]);
+      lds_load16(v ? Vr : Kr, lds + dst + (wave_s + t * kWaves) * 1024, base + ld_off[t]);
   };
   // Does every row of the wave see every key of tile j?
   auto full_tile = [&](int j) {
@@ -227,12 +232,17 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   float m = -INFINITY, l = 0.0f;
-  floatx16 s[2];      // scores of the tile being worked on
-  bf16x8 pp[2][2];    // probabilities of the previous tile (value product pending)
+  // Scores and probabilities, double-buffered by tile parity: iteration j reads the scores
+  // S[j] from sc[j & 1] and P[j-1] from pr[(j-1) & 1], and writes P[j] into pr[j & 1] and
+  // S[j+1] into sc[(j+1) & 1]. With the parity a compile-time constant (the key loop is
+  // unrolled by two), the roles swap without register copies and every LDS buffer offset
+  // is an instruction immediate.
+  floatx16 sc[2][2];
+  bf16x8 pr[2][2][2];
 
-  // S^T = K[j] Q^T over this wave's score channels, into `d`.
-  auto qk_into = [&](int j, floatx16(&d)[2]) {
-    const lds_char* kb_ = lds + k_buf(j);
+  // S^T = K Q^T from the K buffer at byte offset KOFF, into `d`.
+  auto qk_into = [&](auto koff_c, floatx16(&d)[2]) {
+    constexpr int KOFF = decltype(koff_c)::value;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -240,28 +250,26 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
 #pragma unroll
       for (int kk = 0; kk < NQ; ++kk) {
         const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-            kb_ + kb * 32 * ROWB + k_off[kk]);
+            lds + k_off[kk] + (KOFF + kb * 32 * ROWB));
         d[kb] = mfma32(a, qf[kk], d[kb]);
       }
     }
   };
-  auto qk = [&](int j) { qk_into(j, s); };
-  // O^T += V[j]^T P^T.
-  auto pv = [&](int j, const bf16x8 (&p)[2][2]) {
-    lds_char* vb = lds + v_buf(j);
+  // O^T += V^T P^T from the V buffer at byte offset VOFF.
+  auto pv = [&](auto voff_c, const bf16x8(&p)[2][2]) {
+    constexpr int VOFF = decltype(voff_c)::value;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int roff = (kb * 32 + 16 * h) * ROWB;
           const shortx4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               reinterpret_cast<__attribute__((address_space(3))) shortx4*>(
-                  vb + roff + v_off[db][0]));
+                  lds + v_off[db][0] + (VOFF + (kb * 32 + 16 * h) * ROWB)));
           const shortx4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               reinterpret_cast<__attribute__((address_space(3))) shortx4*>(
-                  vb + roff + v_off[db][1]));
+                  lds + v_off[db][1] + (VOFF + (kb * 32 + 16 * h) * ROWB)));
           // One whole-vector shuffle and one bit cast: assembling the operand element by
           // element (bf16 from 16-bit integers) was lowered to a wrong byte permutation.
           const bf16x8 a = __builtin_bit_cast(
@@ -269,7 +277,7 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
           o[db] = mfma32(a, p[kb][h], o[db]);
         }
   };
-  auto mask = [&](int j) {
+  auto mask = [&](int j, floatx16(&x)[2]) {
     const int k0 = j * BN;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -278,23 +286,23 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
         const int kj = k0 + kb * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
         bool vis = kj <= qi;
         if (kSlide) vis = vis && (qi - kj < window);
-        if (!vis) s[kb][r] = -INFINITY;
+        if (!vis) x[kb][r] = -INFINITY;
       }
   };
-  auto row_max = [&]() {
-    float t0 = max3(s[0][0], s[0][1], s[0][2]);
-    float t1 = max3(s[1][0], s[1][1], s[1][2]);
+  auto row_max = [&](const floatx16(&x)[2]) {
+    float t0 = vmax3(x[0][0], x[0][1], x[0][2]);
+    float t1 = vmax3(x[1][0], x[1][1], x[1][2]);
 #pragma unroll
     for (int r = 3; r < 15; r += 2) {
-      t0 = max3(t0, s[0][r], s[0][r + 1]);
-      t1 = max3(t1, s[1][r], s[1][r + 1]);
+      t0 = vmax3(t0, x[0][r], x[0][r + 1]);
+      t1 = vmax3(t1, x[1][r], x[1][r + 1]);
     }
-    t0 = max3(t0, s[0][15], t1);
-    t0 = __builtin_fmaxf(t0, s[1][15]);
+    t0 = vmax3(t0, x[0][15], t1);
+    t0 = vmax3(t0, x[1][15], x[1][15]);
     return xhalf_max(t0);
   };
   // Probabilities exp2(c (s - m)) rounded to bf16 into `p`; their sum added to l.
-  auto exps = [&](bf16x8 (&p)[2][2]) {
+  auto exps = [&](const floatx16(&x)[2], bf16x8(&p)[2][2]) {
     const float mc = (m == -INFINITY) ? 0.0f : m * c;
     bf16x2 ones;
     ones[0] = (__bf16)1.0f;
@@ -306,12 +314,18 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           bf16x2 q2;
-          q2[0] = (__bf16)fast_exp2(__builtin_fmaf(s[kb][h * 8 + e], c, -mc));
-          q2[1] = (__bf16)fast_exp2(__builtin_fmaf(s[kb][h * 8 + e + 1], c, -mc));
+          q2[0] = (__bf16)fast_exp2(__builtin_fmaf(x[kb][h * 8 + e], c, -mc));
+          q2[1] = (__bf16)fast_exp2(__builtin_fmaf(x[kb][h * 8 + e + 1], c, -mc));
           p[kb][h][e] = q2[0];
           p[kb][h][e + 1] = q2[1];
           l = __builtin_amdgcn_fdot2_f32_bf16(q2, ones, l, false);
         }
+  };
+  auto scale_o = [&](float f) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= f;
   };
 
   // ---- prologue: zero both V buffers (the first iteration multiplies P = 0 by the buffer
@@ -323,41 +337,42 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
     for (int i = tid; i < 2 * TILEB / 16; i += kWaves * kWave) vz[i] = z;
   }
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pp[kb][h][e] = (__bf16)0.0f;
-  load_tile(false, k_buf(lo), lo);
-  if (lo + 1 <= hi) load_tile(false, k_buf(lo + 1), lo + 1);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pr[t][kb][h][e] = (__bf16)0.0f;
+  load_tile(false, (lo & 1) * TILEB, lo);
+  if (lo + 1 <= hi) load_tile(false, ((lo + 1) & 1) * TILEB, lo + 1);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
-  qk(lo);
+  if (lo & 1)
+    qk_into(std::integral_constant<int, TILEB>{}, sc[1]);
+  else
+    qk_into(std::integral_constant<int, 0>{}, sc[0]);
   __syncthreads();
 
   // ---- key loop. Every wave runs the same sequence on every tile of the workgroup's
   // range: keys a wave cannot see are masked (probability 0, softmax state unchanged), so
   // the loop body is one straight path and the register allocation stays within two waves
   // per SIMD.
-  float alpha_p = 1.0f;   // pending rescale of O, decided on the previous tile
+  float alpha_p = 1.0f;  // pending rescale of O, decided on the previous tile
   bool moved_p = false;
-  for (int j = lo; j <= hi; ++j) {
-    // Loads for the next iteration: K[j+2] into K's buffer j & 1 (K[j] was read during
-    // iteration j-1) and V[j] into V's buffer j & 1 (V[j-2] was read during j-1).
-    if (j + 2 <= hi) load_tile(false, k_buf(j), j + 2);
-    load_tile(true, v_buf(j), j);
-
+  // One iteration on tile j, with PAR = j & 1.
+  auto iter = [&](auto par_c, int j) {
+    constexpr int PAR = decltype(par_c)::value;
+    // Loads for the next iteration: K[j+2] into K's buffer PAR (K[j] was read during
+    // iteration j-1) and V[j] into V's buffer PAR (V[j-2] was read during j-1).
+    if (j + 2 <= hi) load_tile(false, PAR * TILEB, j + 2);
+    load_tile(true, (2 + PAR) * TILEB, j);
     // Rescale decided on tile j-1: O holds tiles up to j-2 here, and the value product of
     // tile j-1 below is already on tile j-1's reference.
-    if (moved_p) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha_p;
-    }
-    if (!full_tile(j)) mask(j);
+    if (moved_p) scale_o(alpha_p);
+    if (!full_tile(j)) mask(j, sc[PAR]);
     // Reference move for tile j (rare): m and l follow at once, O at the next iteration.
-    const float tmax = row_max();
+    const float tmax = row_max(sc[PAR]);
     float alpha = 1.0f;
     const bool moved = __any(tmax > m + gap);
     if (moved) {
@@ -371,14 +386,12 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
     // The group barriers fix the issue order so that vector work sits between the matrix
     // instructions: a wave issues in order, and an MFMA waiting for the busy matrix pipe
     // holds up everything behind it.
-    bf16x8 pn[2][2];
-    floatx16 sn[2];
-    pv(j - 1, pp);
-    exps(pn);
-    qk_into(j + 1, sn);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
+    pv(std::integral_constant<int, (3 - PAR) * TILEB>{}, pr[1 - PAR]);
+    exps(sc[PAR], pr[PAR]);
+    qk_into(std::integral_constant<int, (1 - PAR) * TILEB>{}, sc[1 - PAR]);
     constexpr int kMfma = DB * 4 + 2 * NQ;  // matrix instructions in the block
     constexpr int kValu = 96 / kMfma + 1;   // vector instructions between two of them
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
 #pragma unroll
     for (int i = 0; i < kMfma / 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
@@ -388,24 +401,22 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
     }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = sn[kb];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) pp[kb][h] = pn[kb][h];
-    }
     alpha_p = alpha;
     moved_p = moved;
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
+  };
+  int j = lo;
+  if (j & 1) iter(std::integral_constant<int, 1>{}, j++);
+  for (; j <= hi; j += 2) {
+    iter(std::integral_constant<int, 0>{}, j);
+    if (j + 1 <= hi) iter(std::integral_constant<int, 1>{}, j + 1);
   }
-  if (moved_p) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha_p;
-  }
-  pv(hi, pp);
+  if (moved_p) scale_o(alpha_p);
+  if (hi & 1)
+    pv(std::integral_constant<int, 3 * TILEB>{}, pr[1]);
+  else
+    pv(std::integral_constant<int, 2 * TILEB>{}, pr[0]);
 
   // ---- epilogue: out = O / l; differential: O1 / l1 - lambda * O2 / l2 with map 1's term
   // passed to map 0 through LDS. Element (db, r) of a lane is channel
