@@ -85,22 +85,43 @@ __device__ __forceinline__ int swz(int r) {
     return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-// 16 bytes per lane from buffer offset `voff` of `r` into LDS at dst + 16 * lane (dst is
-// wave-uniform); offsets outside the buffer's range write zeros. The builtin is compiled in
-// the device pass only: seen by the host pass inside a kernel template, it makes that pass
-// drop the kernel's launch stub.
-__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, lds_char* dst, int voff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
-#endif
+// Buffer descriptor words (base, stride 0, num_records = bytes, raw-buffer flags): loads
+// at byte offsets >= bytes return zeros.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 rsrc_words(unsigned long long base, int bytes) {
+  u32x4 r;
+  r[0] = (unsigned)base;
+  r[1] = (unsigned)(base >> 32) & 0xffffu;
+  r[2] = (unsigned)(bytes > 0 ? bytes : 0);
+  r[3] = 0x00020000u;
+  return r;
 }
 
-// max(a, b, c) in one v_max3_f32. The operands are finite or -inf (scores, masked scores),
-// never NaN, so the input canonicalization that fmaxf implies is not needed.
+// 16 bytes per lane from offset `voff` of buffer `r` into LDS at lds_base + 16 * lane
+// (lds_base wave-uniform, in M0); offsets outside the buffer write zeros. Written as
+// assembly so that the compiler does not see an LDS store: it would otherwise order every
+// later LDS read of the block after these loads and wait for them. Completion is the
+// kernel's business: every tile is read only after an s_waitcnt vmcnt(0) and a barrier that
+// follow its loads, and no compiler-visible vector load is in flight inside the key loop.
+// `voff` must be a register that is never rewritten while loads are in flight (the
+// per-tile step lives in the descriptor): the address operand of a load inside inline
+// assembly gets no hazard protection from the compiler.
+__device__ __forceinline__ void lds_load16(const u32x4& r, unsigned lds_base, int voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_base), "v"(voff), "s"(r)
+      : "memory", "m0");
+}
+
+// max(a, b, c): one v_max3_f32. This file is compiled with -fno-honor-nans (no NaN reaches
+// a value the kernel uses: scores are finite or masked to -inf), so fmaxf needs no input
+// canonicalization. (Not inline assembly: a vector read of an MFMA result needs wait states
+// that the compiler inserts only for instructions it can see.)
 __device__ __forceinline__ float vmax3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+  return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
 }
 
 // Value of lane ^ 32 next to the lane's own: returns (own, other) combined by `op`.
@@ -142,6 +163,7 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   constexpr int kSmem = (4 * TILEB > kXchBytes) ? 4 * TILEB : kXchBytes;
   __shared__ __attribute__((aligned(1024))) char smem[kSmem];
   lds_char* const lds = (lds_char*)(smem);
+  const unsigned lds_addr = (unsigned)(uintptr_t)lds;  // LDS byte address of smem
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -160,8 +182,8 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   const size_t head = (size_t)bh * (size_t)L * D;
   const int head_bytes = L * ROWB;
   const __amdgpu_buffer_rsrc_t Qr = make_rsrc(qg + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t Kr = make_rsrc(kg + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t Vr = make_rsrc(vg + head, head_bytes);
+  const unsigned long long Kbase = reinterpret_cast<unsigned long long>(kg + head);
+  const unsigned long long Vbase = reinterpret_cast<unsigned long long>(vg + head);
 
   const float c = kLog2e / __builtin_sqrtf(kDiff ? (float)(D / 2) : (float)D);
   const float gap = kRescaleLog2Gap / c;
@@ -212,11 +234,14 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
 
   // LDS byte offsets of the K and V buffers holding tile j.
   // Tile j of K (v = false) or V (v = true) into the LDS buffer at byte offset `dst`.
+  // The descriptor starts at the tile (scalar arithmetic), so the per-lane offsets ld_off
+  // stay the same for every tile.
   auto load_tile = [&](bool v, int dst, int j) {
-    const int base = j * TILEB;
+    const u32x4 r = rsrc_words((v ? Vbase : Kbase) + (unsigned long long)j * TILEB,
+                               head_bytes - j * TILEB);
 #pragma unroll
     for (int t = 0; t < NIW; ++t)
-      lds_load16(v ? Vr : Kr, lds + dst + (wave_s + t * kWaves) * 1024, base + ld_off[t]);
+      lds_load16(r, (unsigned)(lds_addr + dst + (wave_s + t * kWaves) * 1024), ld_off[t]);
   };
   // Does every row of the wave see every key of tile j?
   auto full_tile = [&](int j) {
@@ -329,7 +354,8 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   };
 
   // ---- prologue: zero both V buffers (the first iteration multiplies P = 0 by the buffer
-  // of tile lo-1, which must hold finite values); K[lo], K[lo+1] into LDS; S = K[lo] Q^T.
+  // of tile lo-1, which must hold finite values); K[lo], K[lo+1] into LDS; S = K[lo] Q^T
+  // and its row max.
   {
     const floatx4 z = {0.0f, 0.0f, 0.0f, 0.0f};
     floatx4* const vz = reinterpret_cast<floatx4*>(smem + 2 * TILEB);
@@ -345,13 +371,17 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
 #pragma unroll
         for (int e = 0; e < 8; ++e) pr[t][kb][h][e] = (__bf16)0.0f;
   load_tile(false, (lo & 1) * TILEB, lo);
-  if (lo + 1 <= hi) load_tile(false, ((lo + 1) & 1) * TILEB, lo + 1);
+  load_tile(false, ((lo + 1) & 1) * TILEB, lo + 1);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
-  if (lo & 1)
+  float tmax_n;  // row max of the scores of the next tile (unmasked)
+  if (lo & 1) {
     qk_into(std::integral_constant<int, TILEB>{}, sc[1]);
-  else
+    tmax_n = row_max(sc[1]);
+  } else {
     qk_into(std::integral_constant<int, 0>{}, sc[0]);
+    tmax_n = row_max(sc[0]);
+  }
   __syncthreads();
 
   // ---- key loop. Every wave runs the same sequence on every tile of the workgroup's
@@ -363,16 +393,23 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   // One iteration on tile j, with PAR = j & 1.
   auto iter = [&](auto par_c, int j) {
     constexpr int PAR = decltype(par_c)::value;
-    // Loads for the next iteration: K[j+2] into K's buffer PAR (K[j] was read during
-    // iteration j-1) and V[j] into V's buffer PAR (V[j-2] was read during j-1).
-    if (j + 2 <= hi) load_tile(false, PAR * TILEB, j + 2);
+    // Loads for the next iteration, issued first: K[j+2] into K's buffer PAR (K[j] was read
+    // during iteration j-1) and V[j] into V's buffer PAR (V[j-2] was read during j-1). On
+    // the last tiles the K load falls outside the workgroup's range: it reads zeros or keys
+    // nobody uses, into a buffer that is not read for a real tile again.
+    load_tile(false, PAR * TILEB, j + 2);
     load_tile(true, (2 + PAR) * TILEB, j);
     // Rescale decided on tile j-1: O holds tiles up to j-2 here, and the value product of
     // tile j-1 below is already on tile j-1's reference.
     if (moved_p) scale_o(alpha_p);
-    if (!full_tile(j)) mask(j, sc[PAR]);
+    // Row max of tile j: taken during the previous iteration, again here after the mask
+    // on tiles that cross the diagonal or the window edge.
+    float tmax = tmax_n;
+    if (!full_tile(j)) {
+      mask(j, sc[PAR]);
+      tmax = row_max(sc[PAR]);
+    }
     // Reference move for tile j (rare): m and l follow at once, O at the next iteration.
-    const float tmax = row_max(sc[PAR]);
     float alpha = 1.0f;
     const bool moved = __any(tmax > m + gap);
     if (moved) {
@@ -381,17 +418,19 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
       l *= alpha;
       m = m_new;
     }
-    // One straight block: O += V[j-1] P[j-1], the exponentials of tile j and
-    // S[j+1] = K[j+1] Q^T (on the last tile it reads a stale buffer and is discarded).
-    // The group barriers fix the issue order so that vector work sits between the matrix
+    // One straight block: S[j+1] = K[j+1] Q^T first, then O += V[j-1] P[j-1]; beside
+    // them the exponentials of tile j and, once S[j+1] is in, its row max (on the last
+    // tile the scores of tile hi+1 come from a stale buffer and are discarded). The group
+    // barriers fix the issue order so that vector work sits between the matrix
     // instructions: a wave issues in order, and an MFMA waiting for the busy matrix pipe
     // holds up everything behind it.
+    qk_into(std::integral_constant<int, (1 - PAR) * TILEB>{}, sc[1 - PAR]);
     pv(std::integral_constant<int, (3 - PAR) * TILEB>{}, pr[1 - PAR]);
     exps(sc[PAR], pr[PAR]);
-    qk_into(std::integral_constant<int, (1 - PAR) * TILEB>{}, sc[1 - PAR]);
+    tmax_n = row_max(sc[1 - PAR]);
     constexpr int kMfma = DB * 4 + 2 * NQ;  // matrix instructions in the block
     constexpr int kValu = 96 / kMfma + 1;   // vector instructions between two of them
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
 #pragma unroll
     for (int i = 0; i < kMfma / 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
