@@ -39,8 +39,10 @@ PEAK_BF16_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
 VARIANT_NAMES = ("full", "sliding", "differential")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+# Sources of the bf16 kernel the bench times (a traffic summary is valid only for them).
 KERNEL_SOURCES = [os.path.join(ROOT, "heterogeneous_attention_mixer_amd", "csrc", f)
-                  for f in ("attn_prefill.hip", "kernels.h")]
+                  for f in ("attn_prefill_dma.hip", "device_common.h", "kernels.h")]
+KERNEL_NAME = "prefill_dma_kernel"
 
 
 def visible_pairs(variant: str, L: int, window: int) -> int:
@@ -103,7 +105,7 @@ def write_traffic(fetch_csv: str, write_csv: str, command: str) -> str:
                     continue
                 name = r["Kernel_Name"]
                 key = next((v for k, v in KERNEL_VARIANT_TAGS.items()
-                            if "prefill_kernel" in name and k in name and "DF16b" in name),
+                            if KERNEL_NAME in name and k in name),
                            "copy" if "copyBuffer" in name else None)
                 if key:
                     out.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
@@ -115,7 +117,7 @@ def write_traffic(fetch_csv: str, write_csv: str, command: str) -> str:
         raise SystemExit("no copy-kernel calibration in the counter files")
     fscale = COPY_BYTES / fetch["copy"]
     wscale = COPY_BYTES / write["copy"]
-    lines = ["# HBM bytes per launch of prefill_kernel<128, variant, bf16> at B=1 H=16 L=8192",
+    lines = [f"# HBM bytes per launch of {KERNEL_NAME}<128, variant> at B=1 H=16 L=8192",
              "# (Latin stack workload), from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE,",
              "# each scaled by what it reads for a plain 256 MiB device copy.",
              f"# command: {command}",
@@ -296,7 +298,7 @@ def main(argv=None) -> int:
     achieved = dom["useful_tflops"]
     roofline = {
         "bound": "mfma",
-        "kernel": f"prefill_kernel<128, {dominant}, bf16>",
+        "kernel": f"{KERNEL_NAME}<128, {dominant}> (bf16)",
         "achieved": achieved,
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
