@@ -106,14 +106,20 @@ __device__ __forceinline__ u32x4 rsrc_words(unsigned long long base, int bytes) 
 // `voff` must be a register that is never rewritten while loads are in flight (the
 // per-tile step lives in the descriptor): the address operand of a load inside inline
 // assembly gets no hazard protection from the compiler.
+// M0 (which the load reads as its LDS base) is saved and restored around it: the compiler
+// reserves M0 and may rely on its value, so it must not change across the statement.
 __device__ __forceinline__ void lds_load16(const u32x4& r, unsigned lds_base, int voff) {
+  unsigned saved;
   asm volatile(
-      "s_mov_b32 m0, %0\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
-      :
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0"
+      : "=&s"(saved)
       : "s"(lds_base), "v"(voff), "s"(r)
-      : "memory", "m0");
+      : "memory");
 }
 
 // max(a, b, c): one v_max3_f32. This file is compiled with -fno-honor-nans (no NaN reaches
