@@ -62,6 +62,17 @@ def make_qkv(seed: int, B: int, H: int, L: int, d: int, dtype: str = "bf16") -> 
     return LayerInputs(vals[0], vals[1], vals[2], bits[0], bits[1], bits[2], "bf16")
 
 
+def make_qkv_gqa(seed: int, B: int, H: int, Hkv: int, L: int, d: int) -> LayerInputs:
+    """Grouped key/value heads: q [B, H, L, d], then k and v [B, Hkv, L, d], drawn in that
+    order from ``default_rng(seed)`` and rounded to bf16 as in ``make_qkv``."""
+    rng = np.random.default_rng(seed)
+    draws = [rng.standard_normal(shape, dtype=np.float32)
+             for shape in ((B, H, L, d), (B, Hkv, L, d), (B, Hkv, L, d))]
+    bits = [round_to_bf16_bits(x) for x in draws]
+    vals = [bf16_bits_to_f32(b) for b in bits]
+    return LayerInputs(vals[0], vals[1], vals[2], bits[0], bits[1], bits[2], "bf16")
+
+
 # Named workloads (seed, variant, window, lambda, B, H, L, d, dtype).
 WORKLOADS = {
     "full_fp32_L256_d64": dict(seed=1, variant="full", window=0, lam=0.0,
@@ -79,6 +90,10 @@ WORKLOADS = {
     "differential_L32768": dict(seed=4, variant="differential", window=0, lam=0.8,
                                 B=1, H=16, L=32768, d=128, dtype="bf16"),
 }
+
+# The model's own attention shape (Table 2, sec. 4.1: 16 heads over 4 KV heads, head_dim
+# 128) at 8K, each variant drawn from seed 600 + variant number.
+GQA = dict(B=1, H=16, Hkv=4, L=8192, d=128, window=1024, lam=0.8, seed0=600)
 
 # The 3x3 Latin stack: base row [full, sliding, differential], window 1024, lambda 0.8,
 # B=1, H=16, L=8192, d=128, bf16, layer l drawn from seed 500 + l.

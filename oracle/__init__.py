@@ -8,10 +8,13 @@ imports the product.
 Contents
   * ``prefill`` / ``prefill_rows`` / ``attention_general``: ctypes wrappers of the fp64 C
     loops in ``oracle.c`` (the attention definition written out per query row).
+  * ``prefill_rows_gqa``: the same layer with key/value heads shared by groups of query
+    heads (Table 2, sec. 4.1).
   * ``latin``: the Latin-square schedule definitions in plain Python.
 
 Source: "Placement Is Free, Composition Is Not: The Latin Square as a Provably-Balanced
-Construction for Heterogeneous Sequence-Mixer Stacks" (Table 1, sec. 3.2, sec. 8, Table 7).
+Construction for Heterogeneous Sequence-Mixer Stacks" (Table 1, sec. 3.2, sec. 4.1 Table 2,
+sec. 8, Table 7).
 """
 from __future__ import annotations
 
@@ -110,6 +113,27 @@ def prefill_rows(q, k, v, variant, window: int = 0, lam: float = 0.0, rows=None,
         raise ValueError(f"oracle rejected arguments (variant={variant}, window={window}, "
                          f"shape={q.shape}, rows={rows is not None})")
     return out
+
+
+def prefill_rows_gqa(q, k, v, variant, window: int = 0, lam: float = 0.0, rows=None,
+                     threads: int = 0) -> np.ndarray:
+    """One mixer layer with grouped key/value heads: q [B, H, L, d], k and v [B, Hkv, L, d]
+    with Hkv dividing H. The model the paper builds uses 16 heads over 4 KV heads (Table 2,
+    sec. 4.1); query head h attends with key/value head h // (H // Hkv), and is otherwise the
+    layer ``prefill_rows`` computes. Written out as exactly that: each key/value head repeated
+    for the H // Hkv query heads that share it, then ``prefill_rows``.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape:
+        raise ValueError(f"q [B, H, L, d], k and v [B, Hkv, L, d]: {q.shape} {k.shape} "
+                         f"{v.shape}")
+    B, H, L, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, L, d) or Hkv < 1 or H % Hkv != 0:
+        raise ValueError(f"k and v must be [B, Hkv, L, d] with Hkv dividing H: {k.shape}")
+    g = H // Hkv
+    return prefill_rows(q, np.repeat(k, g, axis=1), np.repeat(v, g, axis=1), variant, window,
+                        lam, rows, threads)
 
 
 def prefill(q, k, v, variant, window: int = 0, lam: float = 0.0, threads: int = 0):
