@@ -123,8 +123,8 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(Shape<VAR>::threads,
                                amdgpu_waves_per_eu(Shape<VAR>::occupancy,
                                                    Shape<VAR>::occupancy)))
 prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
-               const Tin* __restrict__ vg, Tin* __restrict__ og, int L, int BH, int nq,
-               int window, float lambda) {
+               const Tin* __restrict__ vg, Tin* __restrict__ og, int L, int BH, int G,
+               int nq, int window, float lambda) {
   constexpr bool kDiff = (VAR == kDifferential);
   constexpr bool kSlide = (VAR == kSliding);
   constexpr int kThreads = Shape<VAR>::threads;
@@ -169,11 +169,12 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
   const int q0 = qt * BM;
   const int qw = q0 + rb * 32;    // first query row of this wave
   const int qi = qw + lr;         // this lane's query row
-  const size_t head = (size_t)bh * (size_t)L * D;
+  const size_t head = (size_t)bh * (size_t)L * D;         // q and out
+  const size_t kv_head = (size_t)(bh / G) * (size_t)L * D;  // k and v: G query heads each
   const int head_bytes = L * D * (int)sizeof(Tin);
   const __amdgpu_buffer_rsrc_t Qr = make_rsrc(qg + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t Kr = make_rsrc(kg + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t Vr = make_rsrc(vg + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t Kr = make_rsrc(kg + kv_head, head_bytes);
+  const __amdgpu_buffer_rsrc_t Vr = make_rsrc(vg + kv_head, head_bytes);
 
   const float c = kLog2e / __builtin_sqrtf(kDiff ? (float)(D / 2) : (float)D);
   const float gap = kRescaleLog2Gap / c;
@@ -373,8 +374,8 @@ static hipError_t launch_t(const PrefillLaunch& a, hipStream_t stream) {
   const dim3 grid((unsigned)(BH * nq));
   hipLaunchKernelGGL((prefill_kernel<D, VAR, Tin>), grid, dim3(Shape<VAR>::threads), 0, stream,
                      static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
-                     static_cast<const Tin*>(a.v), static_cast<Tin*>(a.out), a.L, BH, nq,
-                     a.window, a.lambda);
+                     static_cast<const Tin*>(a.v), static_cast<Tin*>(a.out), a.L, BH,
+                     a.H / a.Hkv, nq, a.window, a.lambda);
   return hipGetLastError();
 }
 

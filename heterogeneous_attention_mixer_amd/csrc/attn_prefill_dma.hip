@@ -148,7 +148,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(DShape<VAR>::threads,
                                amdgpu_waves_per_eu(2, 2)))
 prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
                    const __bf16* __restrict__ vg, __bf16* __restrict__ og, int L, int BH,
-                   int nq, int window, float lambda) {
+                   int G, int nq, int window, float lambda) {
   constexpr bool kDiff = (VAR == kDifferential);
   constexpr bool kSlide = (VAR == kSliding);
   constexpr int kWaves = DShape<VAR>::waves;
@@ -185,11 +185,12 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   const int q0 = qt * BM;
   const int qw = q0 + rb * 32;
   const int qi = qw + lr;
-  const size_t head = (size_t)bh * (size_t)L * D;
+  const size_t head = (size_t)bh * (size_t)L * D;         // q and out
+  const size_t kv_head = (size_t)(bh / G) * (size_t)L * D;  // k and v: G query heads each
   const int head_bytes = L * ROWB;
   const __amdgpu_buffer_rsrc_t Qr = make_rsrc(qg + head, head_bytes);
-  const unsigned long long Kbase = reinterpret_cast<unsigned long long>(kg + head);
-  const unsigned long long Vbase = reinterpret_cast<unsigned long long>(vg + head);
+  const unsigned long long Kbase = reinterpret_cast<unsigned long long>(kg + kv_head);
+  const unsigned long long Vbase = reinterpret_cast<unsigned long long>(vg + kv_head);
 
   const float c = kLog2e / __builtin_sqrtf(kDiff ? (float)(D / 2) : (float)D);
   const float gap = kRescaleLog2Gap / c;
@@ -507,7 +508,8 @@ hipError_t launch_dma_t(const PrefillLaunch& a, hipStream_t stream) {
   hipLaunchKernelGGL((prefill_dma_kernel<D, VAR>), dim3((unsigned)(BH * nq)),
                      dim3(DShape<VAR>::threads), 0, stream, static_cast<const __bf16*>(a.q),
                      static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
-                     static_cast<__bf16*>(a.out), a.L, BH, nq, a.window, a.lambda);
+                     static_cast<__bf16*>(a.out), a.L, BH, a.H / a.Hkv, nq, a.window,
+                     a.lambda);
   return hipGetLastError();
 }
 

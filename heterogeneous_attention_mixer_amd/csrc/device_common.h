@@ -94,13 +94,15 @@ __device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// (batch*head, query tile) of workgroup `bid`: heaviest query tiles first; all tiles of a
-// head on XCD (bid mod 8) when the head count is a multiple of 8.
+// (batch*head, query tile) of workgroup `bid`: heaviest query tiles first. Workgroups are
+// dealt to the 8 XCDs round-robin; when the head count is a multiple of 8, XCD (bid mod 8)
+// takes a contiguous block of BH/8 heads, all their query tiles, so that a head's K/V (and
+// that of query heads sharing one K/V head) is served from one L2.
 __device__ __forceinline__ void map_unit(int bid, int BH, int nq, int* bh, int* qt) {
   if ((BH & 7) == 0) {
     const int x = bid & 7, j = bid >> 3, hpx = BH >> 3;
     *qt = nq - 1 - j / hpx;
-    *bh = x + 8 * (j % hpx);
+    *bh = x * hpx + j % hpx;
   } else {
     *bh = bid % BH;
     *qt = nq - 1 - bid / BH;

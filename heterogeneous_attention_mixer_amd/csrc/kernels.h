@@ -8,8 +8,9 @@ namespace mixer {
 
 enum Variant { kFull = 0, kSliding = 1, kDifferential = 2 };
 
-// One validated layer launch. Pointers are device pointers to [B, H, L, d] tensors of
-// bf16 (f32 == false) or fp32 (f32 == true) elements.
+// One validated layer launch. Pointers are device pointers to bf16 (f32 == false) or fp32
+// (f32 == true) tensors: q and out [B, H, L, d], k and v [B, Hkv, L, d]. Query head h of
+// batch b reads K/V head b * Hkv + h / (H / Hkv), i.e. (b * H + h) / (H / Hkv).
 struct PrefillLaunch {
   const void* q;
   const void* k;
@@ -18,7 +19,7 @@ struct PrefillLaunch {
   int variant;
   int window;
   float lambda;
-  int B, H, L, d;
+  int B, H, Hkv, L, d;
   bool f32;
 };
 

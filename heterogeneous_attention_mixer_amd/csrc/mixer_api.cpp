@@ -21,14 +21,17 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-// Host-only checks of one layer; fills `out` on success.
+// Host-only checks of one layer (q and out [B, H, L, d], k and v [B, Hkv, L, d]); fills
+// `out` on success.
 int validate(const void* q, const void* k, const void* v, void* o, int variant, int window,
-             float lambda, int B, int H, int L, int d, bool f32, mixer::PrefillLaunch* out) {
+             float lambda, int B, int H, int Hkv, int L, int d, bool f32,
+             mixer::PrefillLaunch* out) {
   if (!q || !k || !v || !o) return MIXER_EINVAL;
   // The kernels move 16-byte vectors: every tensor must start on a 16-byte boundary.
   for (const void* p : {q, k, v, static_cast<const void*>(o)})
     if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return MIXER_EINVAL;
-  if (B < 1 || H < 1 || L < 1 || d < 1) return MIXER_EINVAL;
+  if (B < 1 || H < 1 || Hkv < 1 || L < 1 || d < 1) return MIXER_EINVAL;
+  if (H % Hkv != 0) return MIXER_EINVAL;
   if (variant != MIXER_FULL && variant != MIXER_SLIDING && variant != MIXER_DIFFERENTIAL)
     return MIXER_EINVAL;
   if (variant == MIXER_SLIDING && window < 1) return MIXER_EINVAL;
@@ -45,7 +48,9 @@ int validate(const void* q, const void* k, const void* v, void* o, int variant, 
   const unsigned __int128 wgs = (unsigned __int128)B * H * mixer::max_grid_units(L);
   if (wgs * 256 >= ((unsigned __int128)1 << 32)) return MIXER_EUNSUPPORTED;
   const size_t bytes = (size_t)elems * esz;
-  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
+  const size_t kv_bytes = bytes / H * Hkv;
+  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, kv_bytes) ||
+      overlaps(o, bytes, v, kv_bytes))
     return MIXER_EINVAL;
   out->q = q;
   out->k = k;
@@ -56,6 +61,7 @@ int validate(const void* q, const void* k, const void* v, void* o, int variant, 
   out->lambda = variant == MIXER_DIFFERENTIAL ? lambda : 0.0f;
   out->B = B;
   out->H = H;
+  out->Hkv = Hkv;
   out->L = L;
   out->d = d;
   out->f32 = f32;
@@ -74,7 +80,16 @@ extern "C" {
 int mixer_prefill_async(const void* q, const void* k, const void* v, void* out, int variant,
                         int window, float lambda, int B, int H, int L, int d, void* stream) {
   mixer::PrefillLaunch a;
-  const int rc = validate(q, k, v, out, variant, window, lambda, B, H, L, d, false, &a);
+  const int rc = validate(q, k, v, out, variant, window, lambda, B, H, H, L, d, false, &a);
+  if (rc != MIXER_OK) return rc;
+  return launch(a, stream);
+}
+
+int mixer_prefill_gqa_async(const void* q, const void* k, const void* v, void* out, int variant,
+                            int window, float lambda, int B, int H, int Hkv, int L, int d,
+                            void* stream) {
+  mixer::PrefillLaunch a;
+  const int rc = validate(q, k, v, out, variant, window, lambda, B, H, Hkv, L, d, false, &a);
   if (rc != MIXER_OK) return rc;
   return launch(a, stream);
 }
@@ -88,7 +103,7 @@ int mixer_prefill_f32_async(const float* q, const float* k, const float* v, floa
                             int variant, int window, float lambda, int B, int H, int L, int d,
                             void* stream) {
   mixer::PrefillLaunch a;
-  const int rc = validate(q, k, v, out, variant, window, lambda, B, H, L, d, true, &a);
+  const int rc = validate(q, k, v, out, variant, window, lambda, B, H, H, L, d, true, &a);
   if (rc != MIXER_OK) return rc;
   return launch(a, stream);
 }
@@ -138,8 +153,8 @@ int mixer_stack_prefill(int N, const int* sched, const void* const* q, const voi
   const int n = N * N;
   std::vector<mixer::PrefillLaunch> layers((size_t)n);
   for (int l = 0; l < n; ++l) {
-    const int rc = validate(q[l], k[l], v[l], out[l], sched[l], window, lambda, B, H, L, d,
-                            false, &layers[(size_t)l]);
+    const int rc = validate(q[l], k[l], v[l], out[l], sched[l], window, lambda, B, H, H, L,
+                            d, false, &layers[(size_t)l]);
     if (rc != MIXER_OK) return rc;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -47,6 +47,7 @@ def lib() -> ctypes.CDLL:
     ip = ctypes.POINTER(ctypes.c_int)
     vpp = ctypes.POINTER(ctypes.c_void_p)
     L.mixer_prefill_async.argtypes = [vp, vp, vp, vp, ci, ci, cf, ci, ci, ci, ci, vp]
+    L.mixer_prefill_gqa_async.argtypes = [vp, vp, vp, vp, ci, ci, cf, ci, ci, ci, ci, ci, vp]
     L.mixer_prefill.argtypes = [vp, vp, vp, vp, ci, ci, cf, ci, ci, ci, ci]
     L.mixer_prefill_f32_async.argtypes = [vp, vp, vp, vp, ci, ci, cf, ci, ci, ci, ci, vp]
     L.mixer_latin_build.argtypes = [ci, ip, ip]
@@ -55,7 +56,8 @@ def lib() -> ctypes.CDLL:
                                       vpp]
     L.mixer_strerror.argtypes = [ci]
     L.mixer_strerror.restype = ctypes.c_char_p
-    for name in ("mixer_prefill_async", "mixer_prefill", "mixer_prefill_f32_async",
+    for name in ("mixer_prefill_async", "mixer_prefill_gqa_async", "mixer_prefill",
+                 "mixer_prefill_f32_async",
                  "mixer_latin_build", "mixer_latin_check", "mixer_stack_prefill"):
         getattr(L, name).restype = ci
     _lib = L
@@ -116,6 +118,35 @@ def mixer_prefill_async(q, k, v, out, variant, window: int = 0, lam: float = 0.0
                                        out.data_ptr(), _variant(variant), int(window),
                                        float(lam), B, H, L, d, s)
     _check(rc, "mixer_prefill_async")
+    return out
+
+
+def mixer_prefill_gqa_async(q, k, v, out, variant, window: int = 0, lam: float = 0.0,
+                            stream=None):
+    """One bf16 layer with grouped key/value heads: q and out [B, H, L, d], k and v
+    [B, Hkv, L, d] with Hkv dividing H. Returns ``out``."""
+    import torch
+    ts = (q, k, v, out)
+    if any(not isinstance(t, torch.Tensor) for t in ts):
+        raise TypeError("q, k, v, out must be torch tensors")
+    if any(t.device.type != "cuda" for t in ts) or len({t.device for t in ts}) != 1:
+        raise MixerError("q, k, v, out must live on one GPU", EINVAL)
+    if any(t.dtype != torch.bfloat16 for t in ts):
+        raise MixerError("q, k, v, out must be torch.bfloat16", EINVAL)
+    if any(t.dim() != 4 for t in ts) or out.shape != q.shape or k.shape != v.shape:
+        raise MixerError("q, out must share [B, H, L, d]; k, v [B, Hkv, L, d]", EINVAL)
+    B, H, L, d = (int(x) for x in q.shape)
+    if k.shape[0] != B or k.shape[2] != L or k.shape[3] != d:
+        raise MixerError("k, v must be [B, Hkv, L, d] with q's B, L and d", EINVAL)
+    if any(not t.is_contiguous() for t in ts):
+        raise MixerError("q, k, v, out must be contiguous", EINVAL)
+    Hkv = int(k.shape[1])
+    s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_of(q)
+    with torch.cuda.device(q.device):
+        rc = lib().mixer_prefill_gqa_async(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                           out.data_ptr(), _variant(variant), int(window),
+                                           float(lam), B, H, Hkv, L, d, s)
+    _check(rc, "mixer_prefill_gqa_async")
     return out
 
 

@@ -9,7 +9,8 @@
  * Conventions shared by every entry point
  *   - Tensors are contiguous row-major [B, H, L, d] device pointers (one head's L x d slice
  *     is contiguous), each starting on a 16-byte boundary. q, k, v and out have the same
- *     shape; H counts query heads and key/value heads alike (multi-head attention).
+ *     shape; H counts query heads and key/value heads alike (multi-head attention), except
+ *     in mixer_prefill_gqa_async, whose k and v have Hkv heads.
  *   - Ownership: the caller allocates and owns every buffer. The library allocates no device
  *     memory, keeps no state between calls and never synchronises the device.
  *   - Asynchrony: the *_async calls and mixer_stack_prefill enqueue work on `stream` (a
@@ -43,7 +44,7 @@ typedef enum {
     MIXER_EINVAL = -1,       /* bad argument: null or unaligned pointer, size < 1, unknown
                                 variant, window < 1 for SLIDING, non-finite lambda for
                                 DIFFERENTIAL, out overlapping q/k/v, size overflow, bad
-                                schedule entry                                             */
+                                schedule entry, Hkv not dividing H                         */
     MIXER_EUNSUPPORTED = -2, /* valid but not built: d not in {64, 128}, one head's L x d
                                 slice of 2 GiB or more, grid too large                     */
     MIXER_ENOTLATIN = -3,    /* mixer_stack_prefill: schedule is not a Latin square          */
@@ -75,6 +76,22 @@ typedef enum {
 int mixer_prefill_async(const void *q, const void *k, const void *v, void *out,
                         int variant, int window, float lambda,
                         int B, int H, int L, int d, void *stream);
+
+/*
+ * mixer_prefill_gqa_async -- the same layer with grouped key/value heads: Hkv key/value heads
+ * shared by H query heads, H / Hkv query heads per key/value head. This is the attention
+ * shape of the model the paper builds (Table 2, sec. 4.1: 16 heads, 4 KV heads, head_dim
+ * 128). Query head h of batch b attends with key/value head b * Hkv + h / (H / Hkv); every
+ * other definition is mixer_prefill_async's (Hkv = H gives exactly that call).
+ *
+ * q, out    [B, H, L, d] bfloat16 device pointers (out written, must not overlap q, k, v).
+ * k, v      [B, Hkv, L, d] bfloat16 device pointers (read only).
+ * Hkv       >= 1 and dividing H; otherwise MIXER_EINVAL.
+ * Other arguments and the return value as for mixer_prefill_async.
+ */
+int mixer_prefill_gqa_async(const void *q, const void *k, const void *v, void *out,
+                            int variant, int window, float lambda,
+                            int B, int H, int Hkv, int L, int d, void *stream);
 
 /* The same layer on the legacy default stream. */
 int mixer_prefill(const void *q, const void *k, const void *v, void *out,

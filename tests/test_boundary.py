@@ -81,6 +81,38 @@ def test_invalid_arguments_rejected_before_launch(lib, kw, code, f32):
     assert _call(lib, f32=f32, **kw) == code
 
 
+def _call_gqa(lib, q=P[0], k=P[1], v=P[2], o=P[3], stream=None, **kw):
+    a = dict(OK_ARGS)
+    a.setdefault("Hkv", None)
+    a.update(kw)
+    hkv = a["H"] if a["Hkv"] is None else a["Hkv"]
+    return lib.mixer_prefill_gqa_async(q, k, v, o, a["variant"], a["window"],
+                                       ctypes.c_float(a["lam"]), a["B"], a["H"], hkv, a["L"],
+                                       a["d"], stream)
+
+
+@pytest.mark.parametrize("kw,code", BAD)
+def test_gqa_entry_rejects_what_the_plain_entry_rejects(lib, kw, code):
+    # With Hkv = H the grouped entry point is the plain one.
+    assert _call_gqa(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw", [
+    dict(H=4, Hkv=0), dict(H=4, Hkv=-2), dict(H=4, Hkv=3), dict(H=2, Hkv=4),
+    dict(H=6, Hkv=4),
+])
+def test_gqa_rejects_kv_heads_that_do_not_divide_the_heads(lib, kw):
+    assert _call_gqa(lib, **kw) == M.EINVAL
+
+
+def test_gqa_overlap_uses_the_smaller_kv_extent(lib):
+    # H=4, Hkv=1, L=64, d=128 bf16: k spans 16 KiB. out starting 16 bytes before its end
+    # overlaps k; q and v are far away.
+    kv_bytes = 1 * 64 * 128 * 2
+    assert _call_gqa(lib, H=4, Hkv=1, o=P[1] + kv_bytes - 16) == M.EINVAL
+    assert _call_gqa(lib, H=4, Hkv=1, o=P[2] + kv_bytes - 16) == M.EINVAL
+
+
 def test_ignored_arguments_do_not_fail_validation_order(lib):
     # window is ignored for FULL and lambda for SLIDING: their bad values must not matter,
     # so these calls reach the next check (null out) and report EINVAL for that.
