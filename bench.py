@@ -16,10 +16,16 @@ Reported (one JSON line):
                   events recorded between the launches inside the timed steps, and the
                   fraction of the dense bf16 MFMA peak;
   roofline        the same for the kernel that takes most of the step time;
+  gqa             one layer per variant at the model's grouped-head shape (16 heads over
+                  4 KV heads, Table 2), timed with HIP events;
   cpu_baseline    the fp64 oracle on the same nine layers, every row (host cores).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       [--copy-calibration] [--sweep]
+Timing starts at the working clock: the GPU lowers its clock while the host draws the
+inputs, so 0.3 s of untimed stack steps (--settle) run before the W warm-up steps, and the
+timed region is exactly the K steps after those.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle SECONDS]
+       [--no-cpu-baseline] [--no-gqa] [--copy-calibration] [--sweep]
 """
 from __future__ import annotations
 
@@ -184,6 +190,12 @@ def main(argv=None) -> int:
                     help="oracle rows per head per layer for the CPU baseline (0 = all)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB device copy first (for HBM counter scaling)")
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of untimed launches before the warm-up steps (and before "
+                         "each sweep point), so that timing starts at the working clock")
+    ap.add_argument("--no-gqa", action="store_true",
+                    help="skip the grouped-head layers (profiling runs whose per-kernel "
+                         "averages must cover the stack's launches only)")
     ap.add_argument("--sweep", action="store_true",
                     help="also time full at L=2K/32K and differential at L=32K")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -243,11 +255,29 @@ def main(argv=None) -> int:
         ks.append(t[1])
         vs.append(t[2])
     outs = [torch.empty_like(q) for q in qs]
+    # Grouped key/value heads at the model's attention shape (Table 2, sec. 4.1: 16 heads
+    # over 4 KV heads): one layer per variant, inputs from seed seed0 + variant number.
+    g = synth.GQA
+    gqa_inputs = []
+    for vi, variant in enumerate(VARIANT_NAMES if not args.no_gqa else ()):
+        inp = synth.make_qkv_gqa(g["seed0"] + vi, g["B"], g["H"], g["Hkv"], g["L"], g["d"])
+        gqa_inputs.append([torch.from_numpy(b).view(torch.bfloat16).to(dev)
+                           for b in (inp.q_bits, inp.k_bits, inp.v_bits)])
     torch.cuda.synchronize()
+
+    def settle(fn, seconds):
+        # The GPU lowers its clock while the host prepares inputs and needs tens of
+        # milliseconds of load to come back: untimed launches until `seconds` have passed.
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(4):
+                fn()
+            torch.cuda.synchronize()
 
     def step(events=None):
         mixer.mixer_stack_prefill(3, sched, qs, ks, vs, outs, W, lam, events=events)
 
+    settle(step, args.settle)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -306,6 +336,32 @@ def main(argv=None) -> int:
         "traffic": read_traffic(dominant),
     }
 
+    # The grouped-head layers, right after the stack (the chip is at its working clock).
+    gqa = {}
+    for vi, variant in enumerate(VARIANT_NAMES if not args.no_gqa else ()):
+        Wg = g["window"] if variant == "sliding" else 0
+        lg = g["lam"] if variant == "differential" else 0.0
+        t = gqa_inputs[vi]
+        o = torch.empty_like(t[0])
+        for _ in range(5):
+            mixer.mixer_prefill_gqa_async(*t, o, variant, Wg, lg)
+        reps = 20
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            mixer.mixer_prefill_gqa_async(*t, o, variant, Wg, lg)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        fl = useful_flops(variant, g["B"], g["H"], g["L"], g["d"], Wg)
+        gqa[variant] = {
+            "ms_per_launch": round(ms, 5),
+            "useful_tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+            "frac_of_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del o
+    del gqa_inputs
+
     sweep = None
     if args.sweep:
         sweep = {}
@@ -316,8 +372,8 @@ def main(argv=None) -> int:
                 t = [torch.from_numpy(b).view(torch.bfloat16).to(dev)
                      for b in (inp.q_bits, inp.k_bits, inp.v_bits)]
                 o = torch.empty_like(t[0])
-                for _ in range(3):
-                    mixer.mixer_prefill_async(*t, o, variant, 0, lam)
+                settle(lambda: mixer.mixer_prefill_async(*t, o, variant, 0, lam),
+                       args.settle)
                 reps = 10 if Lx <= 8192 else 3
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
@@ -365,6 +421,11 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "wall_s_timed": round(t_wall, 4),
+    }
+    line["gqa"] = None if args.no_gqa else {
+        "config": (f"one layer per variant, B={g['B']} H={g['H']} Hkv={g['Hkv']} "
+                   f"L={g['L']} d={g['d']} window={g['window']} lambda={g['lam']}"),
+        "per_variant": gqa,
     }
     if sweep is not None:
         line["sweep"] = sweep
