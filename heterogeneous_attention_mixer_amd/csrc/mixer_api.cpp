@@ -131,7 +131,8 @@ int mixer_latin_check(int N, const int* sched) {
     }
   }
   if ((int)types.size() != N) return 0;
-  // With exactly N types, "once per row" == "no repeat within a row" (same for columns).
+  // With exactly N types, each type appearing once in every row is the same as no repeat
+  // within a row (same for columns).
   for (int r = 0; r < N; ++r)
     for (int c = 0; c < N; ++c)
       for (int c2 = c + 1; c2 < N; ++c2)

@@ -58,10 +58,10 @@ typedef enum {
  *   FULL          out_i = sum_{j <= i} softmax_j(q_i . k_j / sqrt(d)) v_j
  *   SLIDING       as FULL over the keys i - window + 1 <= j <= i (the query counts toward
  *                 the window; window >= L equals FULL; window = 1 returns v)
- *   DIFFERENTIAL  the head dimension is halved ("halves the head dimension"): q1, k1 are
+ *   DIFFERENTIAL  two maps over the two halves of the head dimension: q1, k1 are
  *                 channels [0, d/2), q2, k2 channels [d/2, d); P1, P2 are the causal
- *                 softmax maps of q1 k1^T / sqrt(d/2) and q2 k2^T / sqrt(d/2); the two maps
- *                 are subtracted ("subtracts two attention maps"):
+ *                 softmax maps of q1 k1^T / sqrt(d/2) and q2 k2^T / sqrt(d/2); the second
+ *                 map, weighted by lambda, is taken from the first:
  *                 out_i = sum_{j <= i} (P1_ij - lambda * P2_ij) v_j, v full width d.
  *
  * q, k, v   [B, H, L, d] bfloat16 device pointers (read only).

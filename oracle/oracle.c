@@ -7,8 +7,9 @@
  *
  * Source: "Placement Is Free, Composition Is Not: The Latin Square as a Provably-Balanced
  * Construction for Heterogeneous Sequence-Mixer Stacks".
- *   Table 1 (sec. 3.1): full = exact all-pairs interactions; sliding = local, blind beyond
- *   its window; differential = subtracts two attention maps and halves the head dimension.
+ *   Table 1 (sec. 3.1): full attends every earlier position exactly; sliding sees only a
+ *   local window of recent positions; differential takes the difference of two attention
+ *   maps, each computed over half of the head dimension.
  *   Sec. 8 (causal safety): no mixer may read future positions.
  *   Table 2 (sec. 4.1): heads 16, head_dim 128, bfloat16.
  *
