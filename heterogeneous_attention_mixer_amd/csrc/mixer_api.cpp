@@ -144,17 +144,14 @@ int mixer_latin_check(int N, const int* sched) {
   return 1;
 }
 
-int mixer_stack_prefill(int N, const int* sched, const void* const* q, const void* const* k,
-                        const void* const* v, void* const* out, int window, float lambda,
-                        int B, int H, int L, int d, void* stream, void* const* layer_events) {
-  if (N < 1 || N > kMaxOrder || !sched || !q || !k || !v || !out) return MIXER_EINVAL;
-  const int lc = mixer_latin_check(N, sched);
-  if (lc < 0) return lc;
-  if (lc == 0) return MIXER_ENOTLATIN;
-  const int n = N * N;
+int mixer_layers_prefill(int n, const int* variants, const void* const* q,
+                         const void* const* k, const void* const* v, void* const* out,
+                         int window, float lambda, int B, int H, int L, int d, void* stream,
+                         void* const* layer_events) {
+  if (n < 1 || !variants || !q || !k || !v || !out) return MIXER_EINVAL;
   std::vector<mixer::PrefillLaunch> layers((size_t)n);
   for (int l = 0; l < n; ++l) {
-    const int rc = validate(q[l], k[l], v[l], out[l], sched[l], window, lambda, B, H, H, L,
+    const int rc = validate(q[l], k[l], v[l], out[l], variants[l], window, lambda, B, H, H, L,
                             d, false, &layers[(size_t)l]);
     if (rc != MIXER_OK) return rc;
   }
@@ -173,6 +170,17 @@ int mixer_stack_prefill(int N, const int* sched, const void* const* q, const voi
       return MIXER_EHIP;
   }
   return MIXER_OK;
+}
+
+int mixer_stack_prefill(int N, const int* sched, const void* const* q, const void* const* k,
+                        const void* const* v, void* const* out, int window, float lambda,
+                        int B, int H, int L, int d, void* stream, void* const* layer_events) {
+  if (N < 1 || N > kMaxOrder || !sched || !q || !k || !v || !out) return MIXER_EINVAL;
+  const int lc = mixer_latin_check(N, sched);
+  if (lc < 0) return lc;
+  if (lc == 0) return MIXER_ENOTLATIN;
+  return mixer_layers_prefill(N * N, sched, q, k, v, out, window, lambda, B, H, L, d, stream,
+                              layer_events);
 }
 
 const char* mixer_strerror(int status) {

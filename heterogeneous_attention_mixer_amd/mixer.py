@@ -54,11 +54,14 @@ def lib() -> ctypes.CDLL:
     L.mixer_latin_check.argtypes = [ci, ip]
     L.mixer_stack_prefill.argtypes = [ci, ip, vpp, vpp, vpp, vpp, ci, cf, ci, ci, ci, ci, vp,
                                       vpp]
+    L.mixer_layers_prefill.argtypes = [ci, ip, vpp, vpp, vpp, vpp, ci, cf, ci, ci, ci, ci, vp,
+                                       vpp]
     L.mixer_strerror.argtypes = [ci]
     L.mixer_strerror.restype = ctypes.c_char_p
     for name in ("mixer_prefill_async", "mixer_prefill_gqa_async", "mixer_prefill",
                  "mixer_prefill_f32_async",
-                 "mixer_latin_build", "mixer_latin_check", "mixer_stack_prefill"):
+                 "mixer_latin_build", "mixer_latin_check", "mixer_stack_prefill",
+                 "mixer_layers_prefill"):
         getattr(L, name).restype = ci
     _lib = L
     return L
@@ -203,30 +206,50 @@ def mixer_latin_check(n: int, sched) -> bool:
     return rc == 1
 
 
-def mixer_stack_prefill(n: int, sched, qs, ks, vs, outs, window: int = 0, lam: float = 0.0,
-                        events=None, stream=None):
-    """Runs the n*n layers of a Latin schedule back to back on one stream. ``qs`` .. ``outs``
-    are sequences of n*n bf16 tensors of one shape; ``events`` optionally n*n + 1 recorded
-    ``torch.cuda.Event`` objects that the library re-records around the layers."""
+def _layer_args(m, variants, qs, ks, vs, outs, events):
     import torch
-    m = n * n
-    if not (len(sched) == len(qs) == len(ks) == len(vs) == len(outs) == m):
-        raise MixerError("schedule and tensor lists must hold n*n entries", EINVAL)
+    if not (len(variants) == len(qs) == len(ks) == len(vs) == len(outs) == m):
+        raise MixerError("variant and tensor lists must hold one entry per layer", EINVAL)
     B, H, L, d = _shape(qs[0], ks[0], vs[0], outs[0], torch.bfloat16)
     for t in zip(qs, ks, vs, outs):
         _shape(*t, torch.bfloat16)
         if t[0].shape != qs[0].shape or t[0].device != qs[0].device:
             raise MixerError("every layer must share one shape and device", EINVAL)
     arr = lambda ts: (ctypes.c_void_p * m)(*[t.data_ptr() for t in ts])  # noqa: E731
-    s = (ctypes.c_int * m)(*[_variant(x) for x in sched])
+    s = (ctypes.c_int * m)(*[_variant(x) for x in variants])
     ev = None
     if events is not None:
         if len(events) != m + 1:
-            raise MixerError("events must hold n*n + 1 entries", EINVAL)
+            raise MixerError("events must hold one entry per layer plus one", EINVAL)
         ev = (ctypes.c_void_p * (m + 1))(*[e.cuda_event for e in events])
+    return (B, H, L, d), s, arr(qs), arr(ks), arr(vs), arr(outs), ev
+
+
+def mixer_stack_prefill(n: int, sched, qs, ks, vs, outs, window: int = 0, lam: float = 0.0,
+                        events=None, stream=None):
+    """Runs the n*n layers of a Latin schedule back to back on one stream. ``qs`` .. ``outs``
+    are sequences of n*n bf16 tensors of one shape; ``events`` optionally n*n + 1 recorded
+    ``torch.cuda.Event`` objects that the library re-records around the layers."""
+    import torch
+    (B, H, L, d), s, q, k, v, o, ev = _layer_args(n * n, sched, qs, ks, vs, outs, events)
     st = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_of(qs[0])
     with torch.cuda.device(qs[0].device):
-        rc = lib().mixer_stack_prefill(n, s, arr(qs), arr(ks), arr(vs), arr(outs),
-                                       int(window), float(lam), B, H, L, d, st, ev)
+        rc = lib().mixer_stack_prefill(n, s, q, k, v, o, int(window), float(lam), B, H, L, d,
+                                       st, ev)
     _check(rc, "mixer_stack_prefill")
+    return outs
+
+
+def mixer_layers_prefill(variants, qs, ks, vs, outs, window: int = 0, lam: float = 0.0,
+                         events=None, stream=None):
+    """Runs len(variants) layers of any variants back to back on one stream (no Latin check);
+    arguments as for ``mixer_stack_prefill``."""
+    import torch
+    m = len(variants)
+    (B, H, L, d), s, q, k, v, o, ev = _layer_args(m, variants, qs, ks, vs, outs, events)
+    st = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_of(qs[0])
+    with torch.cuda.device(qs[0].device):
+        rc = lib().mixer_layers_prefill(m, s, q, k, v, o, int(window), float(lam), B, H, L, d,
+                                        st, ev)
+    _check(rc, "mixer_layers_prefill")
     return outs

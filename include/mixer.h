@@ -140,6 +140,24 @@ int mixer_stack_prefill(int N, const int *sched,
                         void *const *out, int window, float lambda,
                         int B, int H, int L, int d, void *stream, void *const *layer_events);
 
+/*
+ * mixer_layers_prefill -- n layers of any variants back to back on one stream, with no
+ * Latin-square check: the runner mixer_stack_prefill uses after its check. It also runs the
+ * other depth orders of one layer multiset, the placement arms of Table 7 (sec. 6.1):
+ * periodic (the same row repeated), block (each type in one band) and the homogeneous
+ * all-FULL reference.
+ *
+ * variants        n mixer_variant values; layer l runs variants[l].
+ * q, k, v, out    host arrays of n device pointers, one [B, H, L, d] bf16 tensor each.
+ * window, lambda, layer_events   as for mixer_stack_prefill (layer_events: n + 1 events).
+ * Every layer's arguments are validated before the first launch. Returns MIXER_OK or the
+ * first layer's error (nothing launched then).
+ */
+int mixer_layers_prefill(int n, const int *variants,
+                         const void *const *q, const void *const *k, const void *const *v,
+                         void *const *out, int window, float lambda,
+                         int B, int H, int L, int d, void *stream, void *const *layer_events);
+
 /* A static, human-readable description of a mixer_status (never NULL). */
 const char *mixer_strerror(int status);
 

@@ -179,6 +179,32 @@ def _stack(lib, sched, n=3, ptrs=None, **kw):
                                    a["H"], a["L"], a["d"], None, None)
 
 
+def _layers_call(lib, variants, ptrs=None, **kw):
+    m = len(variants)
+    base = ptrs or [0x1000000 * (i + 1) for i in range(4 * max(m, 1))]
+    arr = lambda off: (ctypes.c_void_p * max(m, 1))(*base[off * m:(off + 1) * m])  # noqa: E731
+    a = dict(window=1024, lam=0.8, B=1, H=2, L=64, d=128)
+    a.update(kw)
+    return lib.mixer_layers_prefill(m, (ctypes.c_int * max(m, 1))(*variants), arr(0), arr(1),
+                                    arr(2), arr(3), a["window"], ctypes.c_float(a["lam"]),
+                                    a["B"], a["H"], a["L"], a["d"], None, None)
+
+
+def test_layers_runner_validates_every_layer_before_launch(lib):
+    # The general runner takes any order (no Latin check) but every layer's arguments are
+    # checked before anything is launched.
+    assert _layers_call(lib, []) == M.EINVAL                                  # n = 0
+    assert lib.mixer_layers_prefill(3, None, None, None, None, None, 0, ctypes.c_float(0),
+                                    1, 1, 8, 64, None, None) == M.EINVAL
+    assert _layers_call(lib, [0, 0, 0, 1, 1, 1, 2, 2, 3]) == M.EINVAL         # variant 3
+    assert _layers_call(lib, [0, 1, 2] * 3, window=0) == M.EINVAL             # sliding layers
+    assert _layers_call(lib, [0] * 8 + [2], lam=math.nan) == M.EINVAL         # differential
+    ptrs = [0x1000000 * (i + 1) for i in range(36)]
+    ptrs[27 + 7] = ptrs[7]                                                     # out[7] = q[7]
+    assert _layers_call(lib, [0] * 9, ptrs=ptrs) == M.EINVAL
+    assert _layers_call(lib, [0] * 9, d=96) == M.EUNSUPPORTED
+
+
 def test_stack_rejects_non_latin_before_launch(lib):
     assert _stack(lib, [0, 1, 2, 0, 1, 2, 0, 1, 2]) == M.ENOTLATIN       # periodic
     assert _stack(lib, [0, 0, 0, 1, 1, 1, 2, 2, 2]) == M.ENOTLATIN       # block

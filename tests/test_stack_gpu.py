@@ -55,3 +55,28 @@ def test_stack_rejects_non_latin_without_launching():
     assert e.value.status == M.ENOTLATIN
     torch.cuda.synchronize()
     assert all(bool(torch.isnan(o.float()).all()) for o in outs)
+
+
+# The placement arms of Table 7 (sec. 6.1) over the three types built here: one layer multiset
+# in other depth orders, and the homogeneous all-full reference.
+ARMS = {
+    "latin": latin.cyclic_square([0, 1, 2]),
+    "periodic": [0, 1, 2] * 3,
+    "block": [0, 0, 0, 1, 1, 1, 2, 2, 2],
+    "homo_full": [0] * 9,
+}
+
+
+@pytest.mark.parametrize("arm", sorted(ARMS))
+def test_layers_runner_runs_every_arm_as_its_layers(arm):
+    import torch
+    B, H, L, d, W, lam = 1, 4, 300, 128, 100, 0.8
+    variants = ARMS[arm]
+    layers = _layers(9, B, H, L, d, 700)
+    outs = [torch.full_like(t[0], float("nan")) for t in layers]
+    M.mixer_layers_prefill(variants, [t[0] for t in layers], [t[1] for t in layers],
+                           [t[2] for t in layers], outs, W, lam)
+    torch.cuda.synchronize()
+    for i, (t, o) in enumerate(zip(layers, outs)):
+        ref = run_layer(t, NAMES[variants[i]], W, lam)
+        assert torch.equal(o, ref), f"{arm} layer {i}"
