@@ -272,30 +272,36 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   floatx16 sc[2][2];
   bf16x8 pr[2][2][2];
 
-  // S^T = K Q^T from the K buffer at byte offset KOFF, into `d`.
+  // The matrix instructions below alternate between independent accumulators: an MFMA that
+  // accumulates into the result of the one just before it waits for that result (about 44
+  // cycles instead of the 32 the pipe needs), so a wave issuing one chain leaves the pipe
+  // idle between instructions. Each accumulator still sums its terms in the same order.
+  // S^T = K Q^T from the K buffer at byte offset KOFF, into `d`: the two 32-key blocks
+  // alternate.
   auto qk_into = [&](auto koff_c, floatx16(&d)[2]) {
     constexpr int KOFF = decltype(koff_c)::value;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) d[kb][r] = 0.0f;
 #pragma unroll
-      for (int kk = 0; kk < NQ; ++kk) {
+    for (int kk = 0; kk < NQ; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
             lds + k_off[kk] + (KOFF + kb * 32 * ROWB));
         d[kb] = mfma32(a, qf[kk], d[kb]);
       }
-    }
   };
-  // O^T += V^T P^T from the V buffer at byte offset VOFF.
+  // O^T += V^T P^T from the V buffer at byte offset VOFF: the DB channel blocks take turns.
   auto pv = [&](auto voff_c, const bf16x8(&p)[2][2]) {
     constexpr int VOFF = decltype(voff_c)::value;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int db = 0; db < DB; ++db) {
           const shortx4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               reinterpret_cast<__attribute__((address_space(3))) shortx4*>(
                   lds + v_off[db][0] + (VOFF + (kb * 32 + 16 * h) * ROWB)));
@@ -309,15 +315,17 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
           o[db] = mfma32(a, p[kb][h], o[db]);
         }
   };
+  // Element (kb, r) of a lane holds key j*BN + c + 4*lg, with c = kb*32 + 8*(r/4) + r%4 a
+  // compile-time constant. With t = qi - j*BN - 4*lg the key is causal-visible when c <= t,
+  // and inside the window as well when 0 <= t - c < window, one unsigned compare (window >= 1).
   auto mask = [&](int j, floatx16(&x)[2]) {
-    const int k0 = j * BN;
+    const int t = qi - j * BN - 4 * lg;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kj = k0 + kb * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
-        bool vis = kj <= qi;
-        if (kSlide) vis = vis && (qi - kj < window);
+        const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
+        const bool vis = kSlide ? (unsigned)(t - c) < (unsigned)window : c <= t;
         if (!vis) x[kb][r] = -INFINITY;
       }
   };
@@ -447,6 +455,14 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
     }
+    // The probabilities and the row sum are consumed only by the next iteration, so the
+    // compiler may sink their computation past the barrier, out of the block where it hides
+    // under the matrix work: empty statements that read and write them keep it here.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(pr[PAR][kb][h]));
+    asm volatile("" : "+v"(l));
     alpha_p = alpha;
     moved_p = moved;
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
