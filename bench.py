@@ -16,6 +16,11 @@ Reported (one JSON line):
                   events recorded between the launches inside the timed steps, and the
                   fraction of the dense bf16 MFMA peak;
   roofline        the same for the kernel that takes most of the step time;
+  memory          peak device memory of one isolated layer at L = 2K, 8K, 32K: q, k, v and
+                  out, and the drop in free device memory across the launches (0: the
+                  library allocates nothing);
+  arms            step time of the same nine layers in the other depth orders of Table 7
+                  (periodic, block) and as the all-full reference;
   gqa             one layer per variant at the model's grouped-head shape (16 heads over
                   4 KV heads, Table 2), timed with HIP events;
   cpu_baseline    the fp64 oracle on the same nine layers, every row (host cores).
@@ -25,7 +30,7 @@ inputs, so 0.3 s of untimed stack steps (--settle) run before the W warm-up step
 timed region is exactly the K steps after those.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle SECONDS]
-       [--no-cpu-baseline] [--no-gqa] [--copy-calibration] [--sweep]
+       [--no-cpu-baseline] [--no-gqa] [--no-extras] [--copy-calibration] [--sweep]
 """
 from __future__ import annotations
 
@@ -196,6 +201,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-gqa", action="store_true",
                     help="skip the grouped-head layers (profiling runs whose per-kernel "
                          "averages must cover the stack's launches only)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the memory and placement-arm sections (profiling runs, as "
+                         "for --no-gqa)")
     ap.add_argument("--sweep", action="store_true",
                     help="also time full at L=2K/32K and differential at L=32K")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -336,6 +344,67 @@ def main(argv=None) -> int:
         "traffic": read_traffic(dominant),
     }
 
+    # Peak device memory of one isolated layer (Table 3's memory column): the high-water mark
+    # of torch's allocator from before the layer's q/k/v/out exist until all three variants
+    # have run on them, and the drop in the device's free memory across the launches (which
+    # would show any allocation made inside the library).
+    def layer_memory(Lx):
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base_alloc = torch.cuda.memory_allocated(dev)
+        torch.cuda.reset_peak_memory_stats(dev)
+        t = [torch.empty(B, H, Lx, d, dtype=torch.bfloat16, device=dev).normal_()
+             for _ in range(4)]
+        torch.cuda.synchronize()
+        io = torch.cuda.memory_allocated(dev) - base_alloc
+        free0 = torch.cuda.mem_get_info(dev)[0]
+        for variant in VARIANT_NAMES:
+            mixer.mixer_prefill_async(t[0], t[1], t[2], t[3], variant,
+                                      W if variant == "sliding" else 0,
+                                      lam if variant == "differential" else 0.0)
+        torch.cuda.synchronize()
+        res = {"io_bytes": int(io),
+               "high_water_bytes": int(torch.cuda.max_memory_allocated(dev) - base_alloc),
+               "device_free_drop_bytes": int(free0 - torch.cuda.mem_get_info(dev)[0])}
+        del t
+        return res
+
+    memory = (None if args.no_extras
+              else {f"L{Lx}": layer_memory(Lx) for Lx in (2048, 8192, 32768)})
+
+    # The placement arms of Table 7 (sec. 6.1) over the three types built here: the same
+    # nine layers (same inputs per depth) in other orders, and the all-full reference.
+    arm_orders = {
+        "latin": sched,
+        "periodic": base * 3,
+        "block": [x for x in base for _ in range(3)],
+        "homo_full": [0] * n_layers,
+    }
+    # Round-robin over the arms, one step of each per round with events around it, so every
+    # arm sees the same clock state (the chip's clock drifts with load and time).
+    if args.no_extras:
+        arm_orders = {}
+    else:
+        settle(step, args.settle)
+    rounds = 10
+    arm_ev = {arm: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    for _ in range(rounds)] for arm in arm_orders}
+    for arm, order in arm_orders.items():
+        mixer.mixer_layers_prefill(order, qs, ks, vs, outs, W, lam)
+    for r in range(rounds):
+        for arm, order in arm_orders.items():
+            e0, e1 = arm_ev[arm][r]
+            e0.record()
+            mixer.mixer_layers_prefill(order, qs, ks, vs, outs, W, lam)
+            e1.record()
+    torch.cuda.synchronize()
+    arms = {}
+    for arm, order in arm_orders.items():
+        ms = sum(e0.elapsed_time(e1) for e0, e1 in arm_ev[arm]) / rounds
+        fl = sum(useful_flops(VARIANT_NAMES[v], B, H, L, d, W) for v in order)
+        arms[arm] = {"order": "".join("FSD"[v] for v in order), "ms_per_step": round(ms, 5),
+                     "useful_tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
+
     # The grouped-head layers, right after the stack (the chip is at its working clock).
     gqa = {}
     for vi, variant in enumerate(VARIANT_NAMES if not args.no_gqa else ()):
@@ -422,6 +491,8 @@ def main(argv=None) -> int:
         "cpu_baseline": cpu,
         "wall_s_timed": round(t_wall, 4),
     }
+    line["memory"] = memory
+    line["arms"] = arms or None
     line["gqa"] = None if args.no_gqa else {
         "config": (f"one layer per variant, B={g['B']} H={g['H']} Hkv={g['Hkv']} "
                    f"L={g['L']} d={g['d']} window={g['window']} lambda={g['lam']}"),
