@@ -21,6 +21,8 @@ Reported (one JSON line):
                   library allocates nothing);
   arms            step time of the same nine layers in the other depth orders of Table 7
                   (periodic, block) and as the all-full reference;
+  mfma_ceiling    the bf16 matrix-core rate the chip sustains under its power cap on
+                  random operands (nothing but MFMAs), and each variant's share of it;
   gqa             one layer per variant at the model's grouped-head shape (16 heads over
                   4 KV heads, Table 2), timed with HIP events;
   cpu_baseline    the fp64 oracle on the same nine layers, every row (host cores).
@@ -68,6 +70,12 @@ def useful_flops(variant: str, B: int, H: int, L: int, d: int, window: int) -> i
     """4*d flops per visible pair: 2*d for the scores (the differential's two half-width
     maps together also cost 2*d) and 2*d for the weighted sum of values."""
     return 4 * d * B * H * visible_pairs(variant, L, window)
+
+
+def executed_per_useful(variant: str) -> float:
+    """Flops the single-pass kernel executes per useful flop: the differential runs two value
+    products (one per map), 6*d per pair instead of 4*d."""
+    return 1.5 if variant == "differential" else 1.0
 
 
 def kernel_source_hash() -> str:
@@ -323,10 +331,14 @@ def main(argv=None) -> int:
             continue
         ms = sum(ts) / len(ts)
         fl = useful_flops(name, B, H, L, d, W)
+        srt = sorted(ts)
         per_variant[name] = {
             "ms_per_launch": round(ms, 5),
+            "ms_median": round(srt[len(srt) // 2], 5),
+            "ms_min": round(srt[0], 5),
             "launches": len(ts),
             "useful_tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+            "executed_tflops": round(fl * executed_per_useful(name) / (ms * 1e-3) / 1e12, 2),
             "frac_of_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "useful_gflop_per_launch": round(fl / 1e9, 3),
         }
@@ -404,6 +416,43 @@ def main(argv=None) -> int:
         fl = sum(useful_flops(VARIANT_NAMES[v], B, H, L, d, W) for v in order)
         arms[arm] = {"order": "".join("FSD"[v] for v in order), "ms_per_step": round(ms, 5),
                      "useful_tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
+
+    # The matrix-core ceiling under the power cap (a measurement aid): the same bf16 MFMA on
+    # random operands and nothing else, every SIMD busy, so that the prefill kernels can also
+    # be rated against the rate this chip sustains rather than only the 2.4 GHz figure.
+    ceiling = None
+    if not args.no_extras:
+        import numpy as np
+        mc = synth.MFMA_CEILING
+        bits = synth.make_mfma_fragments(mc["seed"], mc["nsets"])
+        frags = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        sink = torch.empty(mc["blocks"] * mixer.CEILING_SINK_PER_BLOCK, dtype=torch.float32,
+                           device=dev)
+
+        def run_ceiling():
+            mixer.mixer_mfma_ceiling_async(frags, sink, mc["blocks"], mc["iters"])
+        settle(run_ceiling, args.settle)
+        reps = 5
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run_ceiling()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        fl = mc["blocks"] * 16 * mc["iters"] * 32 * 32 * 16 * 2
+        ct = fl / (ms * 1e-3) / 1e12
+        ceiling = {"tflops": round(ct, 2), "frac_of_bf16_peak": round(ct / PEAK_BF16_TFLOPS, 4),
+                   "ms_per_launch": round(ms, 5),
+                   "launch": (f"{mc['blocks']} workgroups x 4 waves, each wave 4 chains of "
+                              f"{mc['iters']} v_mfma_f32_32x32x16_bf16 on seeded N(0,1) bf16 "
+                              f"operands")}
+        for pv in per_variant.values():
+            pv["frac_of_measured_ceiling"] = round(pv["useful_tflops"] / ct, 4)
+        roofline["measured_ceiling_tflops"] = ceiling["tflops"]
+        roofline["frac_of_measured_ceiling"] = round(achieved / ct, 4)
+        del frags, sink
 
     # The grouped-head layers, right after the stack (the chip is at its working clock).
     gqa = {}
@@ -493,6 +542,7 @@ def main(argv=None) -> int:
     }
     line["memory"] = memory
     line["arms"] = arms or None
+    line["mfma_ceiling"] = ceiling
     line["gqa"] = None if args.no_gqa else {
         "config": (f"one layer per variant, B={g['B']} H={g['H']} Hkv={g['Hkv']} "
                    f"L={g['L']} d={g['d']} window={g['window']} lambda={g['lam']}"),

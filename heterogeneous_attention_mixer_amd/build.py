@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmixer.so")
 SOURCES = [os.path.join(CSRC, f)
-           for f in ("attn_prefill.hip", "attn_prefill_dma.hip", "mixer_api.cpp")]
+           for f in ("attn_prefill.hip", "attn_prefill_dma.hip", "mfma_ceiling.hip",
+                     "mixer_api.cpp")]
 HEADERS = [os.path.join(CSRC, f) for f in ("kernels.h", "device_common.h")] + [
     os.path.join(ROOT, "include", "mixer.h")]
 

@@ -33,4 +33,11 @@ hipError_t launch_prefill_regstage(const PrefillLaunch& a, hipStream_t stream);
 // Query tiles per (batch, head) for a sequence of L tokens.
 int max_grid_units(int L);
 
+// The matrix-core ceiling measurement (mfma_ceiling.hip): `blocks` workgroups of 4 waves,
+// `iters` (a multiple of 4) instructions per accumulator chain, fragment sets of 8 x 64 x 8
+// bf16 at `frags`, 4 x 16 x 64 floats per wave written to `sink`. Arguments are validated by
+// the caller.
+hipError_t launch_mfma_ceiling(const void* frags, int nsets, float* sink, int blocks, int iters,
+                               hipStream_t stream);
+
 }  // namespace mixer

@@ -183,6 +183,22 @@ int mixer_stack_prefill(int N, const int* sched, const void* const* q, const voi
                               layer_events);
 }
 
+int mixer_mfma_ceiling_async(const void* frags, int nsets, float* sink, int blocks, int iters,
+                             void* stream) {
+  if (!frags || !sink) return MIXER_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(frags) | reinterpret_cast<uintptr_t>(sink)) & 15)
+    return MIXER_EINVAL;
+  if (nsets < 1 || nsets > (1 << 20) || blocks < 1 || blocks > (1 << 20)) return MIXER_EINVAL;
+  if (iters < 4 || iters % 4 != 0) return MIXER_EINVAL;
+  const size_t frag_bytes = (size_t)nsets * 8 * 64 * 16;
+  const size_t sink_bytes = (size_t)blocks * 4 * 4 * 16 * 64 * sizeof(float);
+  if (overlaps(frags, frag_bytes, sink, sink_bytes)) return MIXER_EINVAL;
+  return mixer::launch_mfma_ceiling(frags, nsets, sink, blocks, iters,
+                                    static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MIXER_OK
+             : MIXER_EHIP;
+}
+
 const char* mixer_strerror(int status) {
   switch (status) {
     case MIXER_OK: return "success";

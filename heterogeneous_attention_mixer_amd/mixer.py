@@ -56,12 +56,13 @@ def lib() -> ctypes.CDLL:
                                       vpp]
     L.mixer_layers_prefill.argtypes = [ci, ip, vpp, vpp, vpp, vpp, ci, cf, ci, ci, ci, ci, vp,
                                        vpp]
+    L.mixer_mfma_ceiling_async.argtypes = [vp, ci, vp, ci, ci, vp]
     L.mixer_strerror.argtypes = [ci]
     L.mixer_strerror.restype = ctypes.c_char_p
     for name in ("mixer_prefill_async", "mixer_prefill_gqa_async", "mixer_prefill",
                  "mixer_prefill_f32_async",
                  "mixer_latin_build", "mixer_latin_check", "mixer_stack_prefill",
-                 "mixer_layers_prefill"):
+                 "mixer_layers_prefill", "mixer_mfma_ceiling_async"):
         getattr(L, name).restype = ci
     _lib = L
     return L
@@ -253,3 +254,34 @@ def mixer_layers_prefill(variants, qs, ks, vs, outs, window: int = 0, lam: float
                                         st, ev)
     _check(rc, "mixer_layers_prefill")
     return outs
+
+
+CEILING_SET_ELEMS = 8 * 64 * 8      # bf16 elements per fragment set
+CEILING_SINK_PER_BLOCK = 4 * 4 * 16 * 64  # floats written per workgroup
+
+
+def mixer_mfma_ceiling_async(frags, sink, blocks: int, iters: int, stream=None):
+    """Measurement aid (not part of the method): the matrix-core ceiling kernel.
+    ``frags`` is a contiguous bf16 device tensor holding whole fragment sets (8 x 64 x 8
+    elements each), ``sink`` a contiguous fp32 device tensor of at least
+    blocks * 4 * 4 * 16 * 64 elements. One call executes blocks * 16 * iters MFMAs of
+    32768 flops. Returns ``sink``."""
+    import torch
+    if not (isinstance(frags, torch.Tensor) and isinstance(sink, torch.Tensor)):
+        raise TypeError("frags and sink must be torch tensors")
+    if frags.dtype != torch.bfloat16 or sink.dtype != torch.float32:
+        raise MixerError("frags must be bf16 and sink fp32", EINVAL)
+    if frags.device.type != "cuda" or sink.device != frags.device:
+        raise MixerError("frags and sink must live on one GPU", EINVAL)
+    if not (frags.is_contiguous() and sink.is_contiguous()):
+        raise MixerError("frags and sink must be contiguous", EINVAL)
+    if frags.numel() == 0 or frags.numel() % CEILING_SET_ELEMS:
+        raise MixerError("frags must hold whole fragment sets", EINVAL)
+    if sink.numel() < int(blocks) * CEILING_SINK_PER_BLOCK:
+        raise MixerError("sink is too small for that many workgroups", EINVAL)
+    s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_of(frags)
+    with torch.cuda.device(frags.device):
+        rc = lib().mixer_mfma_ceiling_async(frags.data_ptr(), frags.numel() // CEILING_SET_ELEMS,
+                                            sink.data_ptr(), int(blocks), int(iters), s)
+    _check(rc, "mixer_mfma_ceiling_async")
+    return sink

@@ -74,6 +74,18 @@ def make_qkv_gqa(seed: int, B: int, H: int, Hkv: int, L: int, d: int) -> LayerIn
 
 
 # Named workloads (seed, variant, window, lambda, B, H, L, d, dtype).
+def make_mfma_fragments(seed: int, nsets: int) -> np.ndarray:
+    """Operand fragments for the matrix-core ceiling measurement: ``nsets`` sets of 8
+    fragments x 64 lanes x 8 elements, standard normal draws from ``default_rng(seed)``
+    rounded to bf16 bits (uint16), shape (nsets, 8, 64, 8). Same statistics as q, k, v."""
+    rng = np.random.default_rng(seed)
+    return round_to_bf16_bits(rng.standard_normal((nsets, 8, 64, 8), dtype=np.float32))
+
+
+# The ceiling measurement as the bench runs it: 512 workgroups of 4 waves (two per SIMD),
+# each wave 4 chains of `iters` matrix instructions, about 5 ms per launch at 2 PFLOP/s.
+MFMA_CEILING = dict(blocks=512, iters=36864, nsets=64, seed=700)
+
 WORKLOADS = {
     "full_fp32_L256_d64": dict(seed=1, variant="full", window=0, lam=0.0,
                                B=1, H=2, L=256, d=64, dtype="f32"),

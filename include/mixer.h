@@ -158,6 +158,28 @@ int mixer_layers_prefill(int n, const int *variants,
                          void *const *out, int window, float lambda,
                          int B, int H, int L, int d, void *stream, void *const *layer_events);
 
+/* ---- Measurement aid (not part of the method) ------------------------------------------
+ * The bf16 matrix-core rate the GPU sustains under its power cap when it runs nothing but
+ * v_mfma_f32_32x32x16_bf16, used to rate the prefill kernels beside the data-sheet peak.
+ * `blocks` workgroups of 4 waves; each wave keeps 4 independent accumulator chains of
+ * `iters` instructions each (32*32*16*2 flops per instruction), so one call executes
+ * blocks * 16 * iters * 32768 flops.
+ *
+ * frags   device, bf16, nsets fragment sets of 8 x 64 lanes x 8 elements (8 KiB per set):
+ *         fragments 0-3 are A operands (lane l: row l % 32, k = 8*(l/32) + [0, 8) of a
+ *         32 x 16 matrix), fragments 4-7 are B operands (lane l: column l % 32, the same k).
+ *         Wave w (w = 4 * workgroup + wave) reads set w % nsets. Not written.
+ * sink    device, fp32, blocks * 4 * 4 * 16 * 64 floats, written: chain c of wave w ends
+ *         holding (iters/4) * sum_{u=0..3} A[(u+c)%4] B[(u+2c)%4] (a 32 x 32 matrix); its
+ *         element (i, j) is at sink[((w*4 + c)*16 + r)*64 + lane] with lane = j + 32*((i/4)%2)
+ *         and r = 4*(i/8) + i%4.
+ * Both pointers 16-byte aligned and not overlapping; 1 <= nsets, blocks <= 2^20; iters a
+ * positive multiple of 4. Returns MIXER_OK, MIXER_EINVAL or MIXER_EHIP; asynchronous on
+ * `stream` like the *_async calls.
+ */
+int mixer_mfma_ceiling_async(const void *frags, int nsets, float *sink, int blocks, int iters,
+                             void *stream);
+
 /* A static, human-readable description of a mixer_status (never NULL). */
 const char *mixer_strerror(int status);
 

@@ -227,3 +227,27 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(M, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(M.MixerError):
         M.lib()
+
+
+# ------------------------------------------------ the matrix-core ceiling measurement aid
+
+CEIL_OK = dict(frags=0x10000000, nsets=4, sink=0x20000000, blocks=8, iters=16)
+CEIL_BAD = [
+    dict(frags=None), dict(sink=None), dict(frags=0x10000008), dict(sink=0x20000004),
+    dict(nsets=0), dict(nsets=-1), dict(nsets=(1 << 20) + 1), dict(blocks=0),
+    dict(blocks=(1 << 20) + 1), dict(iters=0), dict(iters=6), dict(iters=-4),
+    # sink (8 workgroups = 512 KiB) starting inside the fragment sets (32 KiB)
+    dict(sink=0x10000000 + 16 * 1024),
+    # fragment sets starting inside the sink
+    dict(frags=0x20000000 + 500 * 1024),
+]
+
+
+@pytest.mark.parametrize("bad", CEIL_BAD)
+def test_ceiling_rejects_bad_arguments(lib, bad):
+    a = dict(CEIL_OK)
+    a.update(bad)
+    rc = lib.mixer_mfma_ceiling_async(a["frags"], a["nsets"], a["sink"], a["blocks"],
+                                      a["iters"], None)
+    assert rc == M.EINVAL, bad
+
