@@ -395,6 +395,5 @@ hipError_t launch_prefill_regstage(const PrefillLaunch& a, hipStream_t stream) {
   return a.d == 64 ? launch_v<64, __bf16>(a, stream) : launch_v<128, __bf16>(a, stream);
 }
 
-int max_grid_units(int L) { return (L + 31) / 32; }  // bm >= 32 for every variant
 
 }  // namespace mixer

@@ -30,8 +30,9 @@ hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream);
 hipError_t launch_prefill_dma(const PrefillLaunch& a, hipStream_t stream);
 hipError_t launch_prefill_regstage(const PrefillLaunch& a, hipStream_t stream);
 
-// Query tiles per (batch, head) for a sequence of L tokens.
-int max_grid_units(int L);
+// An upper bound on the query tiles per (batch, head) of any kernel for a sequence of L
+// tokens (every kernel's query tile holds at least 32 rows); host-side grid-size checks.
+inline int max_grid_units(int L) { return (L + 31) / 32; }
 
 // The matrix-core ceiling measurement (mfma_ceiling.hip): `blocks` workgroups of 4 waves,
 // `iters` (a multiple of 4) instructions per accumulator chain, fragment sets of 8 x 64 x 8
