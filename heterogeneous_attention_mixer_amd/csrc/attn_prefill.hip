@@ -1,4 +1,7 @@
-// attn_prefill.hip -- flash-style causal prefill of one sequence-mixer layer for gfx950.
+// attn_prefill.hip -- flash-style causal prefill of one sequence-mixer layer for gfx950, for
+// fp32 inputs and outputs: K and V are staged through registers, where they are rounded to
+// bf16 on the way into LDS (an LDS DMA cannot convert), and the arithmetic is then that of
+// the bf16 kernel in attn_prefill_dma.hip. Only the small fp32 workload uses it.
 //
 // Variants (Table 1, sec. 3.1 of "Placement Is Free, Composition Is Not: The Latin Square as
 // a Provably-Balanced Construction for Heterogeneous Sequence-Mixer Stacks"):
@@ -42,13 +45,6 @@
 
 #include "device_common.h"
 #include "kernels.h"
-
-#ifndef MIXER_WAVES
-#define MIXER_WAVES 4
-#endif
-#ifndef MIXER_DIFF_ROWS
-#define MIXER_DIFF_ROWS 4
-#endif
 
 namespace mixer {
 
@@ -110,7 +106,7 @@ __device__ __forceinline__ void softmax_step(floatx16 (&s)[2], float& m, float& 
 template <int VAR>
 struct Shape {
   static constexpr int maps = (VAR == kDifferential) ? 2 : 1;
-  static constexpr int rows = (VAR == kDifferential) ? MIXER_DIFF_ROWS : MIXER_WAVES;
+  static constexpr int rows = 4;
   static constexpr int waves = rows * maps;
   static constexpr int threads = waves * kWave;
   static constexpr int bm = 32 * rows;  // query rows per workgroup
@@ -389,10 +385,7 @@ static hipError_t launch_v(const PrefillLaunch& a, hipStream_t stream) {
 }
 
 hipError_t launch_prefill_regstage(const PrefillLaunch& a, hipStream_t stream) {
-  if (a.f32) {
-    return a.d == 64 ? launch_v<64, float>(a, stream) : launch_v<128, float>(a, stream);
-  }
-  return a.d == 64 ? launch_v<64, __bf16>(a, stream) : launch_v<128, __bf16>(a, stream);
+  return a.d == 64 ? launch_v<64, float>(a, stream) : launch_v<128, float>(a, stream);
 }
 
 

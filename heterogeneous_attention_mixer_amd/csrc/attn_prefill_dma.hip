@@ -47,13 +47,6 @@
 #include "device_common.h"
 #include "kernels.h"
 
-#ifndef MIXER_WAVES
-#define MIXER_WAVES 4
-#endif
-#ifndef MIXER_DIFF_ROWS
-#define MIXER_DIFF_ROWS 4
-#endif
-
 namespace mixer {
 
 namespace dma {
@@ -61,12 +54,15 @@ namespace dma {
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-// Launch shape: `rows` blocks of 32 query rows per workgroup; the differential adds a
-// second wave per row block for its second map. Register budget: two waves per SIMD.
+// Launch shape: 4 blocks of 32 query rows per workgroup; the differential adds a second
+// wave per row block for its second map. Register budget: two waves per SIMD, so full and
+// sliding run two workgroups per CU and the differential one. (Two row blocks for the
+// differential, i.e. two 4-wave workgroups per CU, measured slower: twice the K/V bytes
+// moved per flop.)
 template <int VAR>
 struct DShape {
   static constexpr int maps = (VAR == kDifferential) ? 2 : 1;
-  static constexpr int rows = (VAR == kDifferential) ? MIXER_DIFF_ROWS : MIXER_WAVES;
+  static constexpr int rows = 4;
   static constexpr int waves = rows * maps;
   static constexpr int threads = waves * kWave;
   static constexpr int bm = 32 * rows;
@@ -545,11 +541,7 @@ hipError_t launch_prefill_dma(const PrefillLaunch& a, hipStream_t stream) {
 }
 
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream) {
-#ifdef MIXER_BF16_REGSTAGE
-  return launch_prefill_regstage(a, stream);
-#else
   return a.f32 ? launch_prefill_regstage(a, stream) : launch_prefill_dma(a, stream);
-#endif
 }
 
 }  // namespace mixer
