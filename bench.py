@@ -40,6 +40,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -78,11 +79,20 @@ def executed_per_useful(variant: str) -> float:
     return 1.5 if variant == "differential" else 1.0
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without comments and with whitespace runs collapsed: what the compiler
+    sees. String literals in these sources hold no comment markers."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the kernel's code (comments and layout excluded), keying the counter file."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -29,7 +29,9 @@
 //     then computes O += V[j-1] P[j-1] together with the row max of S[j], and the
 //     exponentials of S[j] together with S[j+1] = K[j+1] Q^T; the matrix core and the vector
 //     ALU work on independent data in each half. Two K and two V buffers, one barrier per
-//     tile.
+//     tile. Consecutive matrix instructions alternate between independent accumulators, and
+//     the tile's probabilities are pinned inside the block (see the comments at qk_into and
+//     at the end of the iteration).
 //   * Online softmax in fp32 with exp2 (scale folded with log2 e); the reference max moves
 //     only when a score beats it by more than 2^8 (probabilities stay below 256), so the
 //     accumulator rescale is rare. Row sums are taken over the bf16-rounded probabilities,
