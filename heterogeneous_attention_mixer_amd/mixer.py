@@ -209,6 +209,8 @@ def mixer_latin_check(n: int, sched) -> bool:
 
 def _layer_args(m, variants, qs, ks, vs, outs, events):
     import torch
+    if m < 1:
+        raise MixerError("at least one layer is required", EINVAL)
     if not (len(variants) == len(qs) == len(ks) == len(vs) == len(outs) == m):
         raise MixerError("variant and tensor lists must hold one entry per layer", EINVAL)
     B, H, L, d = _shape(qs[0], ks[0], vs[0], outs[0], torch.bfloat16)

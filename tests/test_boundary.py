@@ -251,3 +251,9 @@ def test_ceiling_rejects_bad_arguments(lib, bad):
                                       a["iters"], None)
     assert rc == M.EINVAL, bad
 
+
+
+def test_binding_rejects_an_empty_layer_list():
+    with pytest.raises(M.MixerError) as e:
+        M.mixer_layers_prefill([], [], [], [], [])
+    assert e.value.status == M.EINVAL
