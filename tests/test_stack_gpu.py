@@ -80,3 +80,31 @@ def test_layers_runner_runs_every_arm_as_its_layers(arm):
     for i, (t, o) in enumerate(zip(layers, outs)):
         ref = run_layer(t, NAMES[variants[i]], W, lam)
         assert torch.equal(o, ref), f"{arm} layer {i}"
+
+
+def test_bench_stack_at_full_size_against_the_oracle(oracle_mod):
+    """The stack exactly as bench.py times it: the nine seeded layers of the workload at
+    B=1, H=16, L=8192, d=128 (W=1024, lambda=0.8) through mixer_stack_prefill, every layer
+    compared with the oracle on sampled rows of every head (each row depends only on its own
+    query and the keys it sees, so sampled rows are exact)."""
+    import torch
+    from heterogeneous_attention_mixer_amd import synth
+    cfg = synth.LATIN_STACK
+    B, H, L, d = cfg["B"], cfg["H"], cfg["L"], cfg["d"]
+    W, lam = cfg["window"], cfg["lam"]
+    base = [list(NAMES.values()).index(x) for x in cfg["base"]]
+    sched = M.mixer_latin_build(base)
+    layers = []
+    for i in range(9):  # one layer's host arrays at a time
+        layers.append(device_tensors(synth.make_qkv(cfg["seed0"] + i, B, H, L, d, "bf16")))
+    outs = [torch.full_like(t[0], float("nan")) for t in layers]
+    M.mixer_stack_prefill(3, sched, [t[0] for t in layers], [t[1] for t in layers],
+                          [t[2] for t in layers], outs, W, lam)
+    torch.cuda.synchronize()
+    del layers
+    rows = sample_rows(L, seed=7, n_random=16, edge=4)
+    for i in range(9):
+        inp = synth.make_qkv(cfg["seed0"] + i, B, H, L, d, "bf16")
+        ref = oracle_mod.prefill_rows(inp.q, inp.k, inp.v, NAMES[sched[i]], W, lam, rows)
+        assert_close(to_f64(outs[i][:, :, rows]), ref, f"bench stack layer {i}")
+        assert not bool(torch.isnan(outs[i].float()).any()), f"layer {i} left rows unwritten"
