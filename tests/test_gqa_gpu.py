@@ -44,6 +44,9 @@ for d in (64, 128):
         SMALL.append(("full", d, B, H, Hkv, L, 0, 0.0))
         SMALL.append(("sliding", d, B, H, Hkv, L, 37, 0.0))
         SMALL.append(("differential", d, B, H, Hkv, L, 0, 0.8))
+# B*H = 64: each XCD takes a block of 8 query heads, i.e. two whole groups of 4.
+for variant, W, lam in (("full", 0, 0.0), ("sliding", 50, 0.0), ("differential", 0, 0.8)):
+    SMALL.append((variant, 128, 2, 32, 8, 200, W, lam))
 
 
 @pytest.mark.parametrize("variant,d,B,H,Hkv,L,W,lam", SMALL)

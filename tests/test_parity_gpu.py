@@ -89,6 +89,23 @@ def test_full_size_sampled_rows(torch_cuda, oracle_mod, name, n_random):
     assert_close(to_f64(out[:, :, rows]), ref, name)
 
 
+# ------------------------------------------- many heads: several heads per XCD block
+
+# B*H a multiple of 8 gives each XCD a contiguous block of B*H/8 heads; the shapes above
+# give it two. These give it 6, 8 and 9, with a ragged sequence length.
+MANY_HEADS = [("full", 2, 24, 1000, 0, 0.0), ("sliding", 2, 32, 777, 200, 0.0),
+              ("differential", 1, 72, 640, 0, 0.8)]
+
+
+@pytest.mark.parametrize("variant,B,H,L,W,lam", MANY_HEADS)
+def test_many_heads_sampled_rows(torch_cuda, oracle_mod, variant, B, H, L, W, lam):
+    inp = make(900 + H, B, H, L, 128)
+    out = run_layer(device_tensors(inp), variant, W, lam)
+    rows = sample_rows(L, seed=H, n_random=24, edge=8)
+    ref = _oracle(oracle_mod, inp, variant, W, lam, rows)
+    assert_close(to_f64(out[:, :, rows]), ref, f"{variant} B={B} H={H} L={L}")
+
+
 # ------------------------------------------------------------------------ invariants
 
 @pytest.mark.parametrize("variant,W,lam,expect", [("full", 0, 0.0, 1.0),
