@@ -106,6 +106,16 @@ def test_many_heads_sampled_rows(torch_cuda, oracle_mod, variant, B, H, L, W, la
     assert_close(to_f64(out[:, :, rows]), ref, f"{variant} B={B} H={H} L={L}")
 
 
+@pytest.mark.parametrize("variant,W,lam", [("full", 0, 0.0), ("sliding", 30, 0.0),
+                                           ("differential", 0, 0.5)])
+def test_many_small_heads_every_row(torch_cuda, oracle_mod, variant, W, lam):
+    """512 (batch, head) slices of 100 tokens, one query tile each: 512 workgroups over a
+    head count that is a multiple of 8 (64 heads per XCD block)."""
+    inp = make(950, 8, 64, 100, 64)
+    out = run_layer(device_tensors(inp), variant, W, lam)
+    assert_close(to_f64(out), _oracle(oracle_mod, inp, variant, W, lam), f"{variant} 8x64 heads")
+
+
 # ------------------------------------------------------------------------ invariants
 
 @pytest.mark.parametrize("variant,W,lam,expect", [("full", 0, 0.0, 1.0),
