@@ -237,9 +237,9 @@ def main(argv=None) -> int:
         return 0
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
-              "supported (the layer shards over batch and heads with no exchange; see the "
-              "design notes)", file=sys.stderr)
+        print(f"bench.py: runs on one GPU; --gpus {args.gpus} is not supported (the layer "
+              "would shard over batch and heads with no exchange, which is not implemented)",
+              file=sys.stderr)
         return 2
 
     import torch

@@ -13,7 +13,7 @@
  *   Sec. 8 (causal safety): no mixer may read future positions.
  *   Table 2 (sec. 4.1): heads 16, head_dim 128, bfloat16.
  *
- * Readings taken where the page is silent (each one is a choice, listed in the design notes):
+ * Readings taken where the page is silent (each one is a choice):
  *   - causal: key j is visible to query i iff j <= i (the diagonal is visible);
  *   - sliding window W counts the query itself: visible iff 0 <= i - j <= W - 1;
  *   - score scale 1/sqrt(d) for full and sliding, 1/sqrt(d/2) for differential;
