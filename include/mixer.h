@@ -117,7 +117,7 @@ int mixer_latin_build(int N, const int *base, int *sched);
 
 /*
  * mixer_latin_check -- 1 if the row-major N x N schedule holds exactly N distinct types and
- * every type appears exactly once in every row and in every column (sec. 1, sec. 3.2),
+ * no type repeats within any row or any column (sec. 1, sec. 3.2),
  * 0 if not, MIXER_EINVAL for N < 1 or a null pointer. Pure host.
  */
 int mixer_latin_check(int N, const int *sched);

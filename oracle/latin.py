@@ -1,7 +1,7 @@
 """Latin-square layer schedules, in plain Python (test infrastructure, see ``oracle``).
 
 Source: "Placement Is Free, Composition Is Not", sec. 1 and sec. 3.2: N mechanisms over N^2
-layers, each mechanism exactly once in every row and every column; Table 7 prints the 4x4
+layers arranged so that no mechanism repeats within a row or within a column; Table 7 prints the 4x4
 proxy schedule row by row ("SGMF GMFS MFSG FSGM"), which is the cyclic left shift of its
 first row, read row-major into layer order.
 """
@@ -16,9 +16,9 @@ def cyclic_square(base):
 
 
 def is_latin(n: int, sched) -> bool:
-    """True iff the flat row-major schedule of n*n entries puts n distinct types in the
-    grid and each type appears exactly once in every row and exactly once in every
-    column."""
+    """True iff the flat row-major schedule of n*n entries holds n distinct types and no
+    type repeats within any row or within any column (so each row and each column holds
+    every type)."""
     if n < 1 or len(sched) != n * n:
         return False
     symbols = set(sched)

@@ -1,7 +1,7 @@
 """Pins of the Latin-square schedule definitions (CPU only).
 
-Source: "Placement Is Free, Composition Is Not", sec. 1 and sec. 3.2 (each type exactly once
-per row and per column), Table 7 (the printed 4x4 proxy schedule and its counter-examples).
+Source: "Placement Is Free, Composition Is Not", sec. 1 and sec. 3.2 (no type repeats within a
+row or a column), Table 7 (the printed 4x4 proxy schedule and its counter-examples).
 """
 import itertools
 import os
