@@ -553,6 +553,10 @@ def main(argv=None) -> int:
     line["memory"] = memory
     line["arms"] = arms or None
     line["mfma_ceiling"] = ceiling
+    if ceiling:
+        # The stack's rate as a share of the rate the same chip sustains on matrix work
+        # alone: steadier across GPUs than the raw value, whose spread is the power cap's.
+        ceiling["stack_value_frac"] = round(value / ceiling["tflops"], 4)
     line["gqa"] = None if args.no_gqa else {
         "config": (f"one layer per variant, B={g['B']} H={g['H']} Hkv={g['Hkv']} "
                    f"L={g['L']} d={g['d']} window={g['window']} lambda={g['lam']}"),
