@@ -22,7 +22,8 @@ Reported (one JSON line):
   arms            step time of the same nine layers in the other depth orders of Table 7
                   (periodic, block) and as the all-full reference;
   mfma_ceiling    the bf16 matrix-core rate the chip sustains under its power cap on
-                  random operands (nothing but MFMAs), and each variant's share of it;
+                  random operands (nothing but MFMAs), with the stack value's share of it
+                  (each variant's share is in per_variant);
   gqa             one layer per variant at the model's grouped-head shape (16 heads over
                   4 KV heads, Table 2), timed with HIP events;
   cpu_baseline    the fp64 oracle on the same nine layers, every row (host cores).
