@@ -116,6 +116,40 @@ def test_many_small_heads_every_row(torch_cuda, oracle_mod, variant, W, lam):
     assert_close(to_f64(out), _oracle(oracle_mod, inp, variant, W, lam), f"{variant} 8x64 heads")
 
 
+# --------------------------------------- key magnitudes that move the reference max
+
+def _scale_keys(inp, factors):
+    """Key j times factors[j], rounded to bf16 again: in place, on both the values the oracle
+    sees and the bits the device receives."""
+    bits = synth.round_to_bf16_bits((inp.k * factors[None, None, :, None]).astype(np.float32))
+    inp.k[...] = synth.bf16_bits_to_f32(bits)
+    inp.k_bits[...] = bits
+
+
+# Rising: later keys score up to 7x higher, so a row's reference max keeps moving past the
+# rescale threshold. Falling: the first keys dominate and later weights underflow. Spikes:
+# every 97th key 12x larger.
+KEY_PROFILES = {
+    "rising": lambda L: 1.0 + 6.0 * np.arange(L) / L,
+    "falling": lambda L: 7.0 - 6.0 * np.arange(L) / L,
+    "spikes": lambda L: np.where(np.arange(L) % 97 == 50, 12.0, 1.0),
+}
+
+
+@pytest.mark.parametrize("profile", sorted(KEY_PROFILES))
+@pytest.mark.parametrize("variant,d,W,lam", [("full", 128, 0, 0.0), ("sliding", 128, 300, 0.0),
+                                             ("differential", 128, 0, 0.8),
+                                             ("full", 64, 0, 0.0),
+                                             ("differential", 64, 0, -0.5)])
+def test_moving_reference_max_every_row(torch_cuda, oracle_mod, profile, variant, d, W, lam):
+    L = 777
+    inp = make(970 + d, 1, 2, L, d)
+    _scale_keys(inp, KEY_PROFILES[profile](L))
+    out = run_layer(device_tensors(inp), variant, W, lam)
+    assert_close(to_f64(out), _oracle(oracle_mod, inp, variant, W, lam),
+                 f"{profile} keys, {variant} d={d}")
+
+
 # ------------------------------------------------------------------------ invariants
 
 @pytest.mark.parametrize("variant,W,lam,expect", [("full", 0, 0.0, 1.0),
