@@ -1,7 +1,9 @@
 // attn_prefill.hip -- flash-style causal prefill of one sequence-mixer layer for gfx950, for
-// fp32 inputs and outputs: K and V are staged through registers, where they are rounded to
-// bf16 on the way into LDS (an LDS DMA cannot convert), and the arithmetic is then that of
-// the bf16 kernel in attn_prefill_dma.hip. Only the small fp32 workload uses it.
+// fp32 inputs and outputs. K and V are staged through registers (an LDS DMA cannot convert).
+// Q and K are split into bf16 high and low parts, and each score is Khi Qhi + Khi Qlo +
+// Klo Qhi on the matrix cores, so the scores keep nearly fp32 accuracy whatever their
+// magnitude; V is rounded to bf16, as the probabilities are. The rest follows the bf16
+// kernel in attn_prefill_dma.hip. Only the small fp32 workload uses it, so it is not tuned.
 //
 // Variants (Table 1, sec. 3.1 of "Placement Is Free, Composition Is Not: The Latin Square as
 // a Provably-Balanced Construction for Heterogeneous Sequence-Mixer Stacks"):
@@ -95,6 +97,24 @@ __device__ __forceinline__ void softmax_step(floatx16 (&s)[2], float& m, float& 
       }
 }
 
+// Eight fp32 values as two bf16 vectors: hi = x rounded to bf16, lo = (x - hi) rounded to
+// bf16. hi + lo equals x to within 2^-16 of |x|, so products of split operands carry scores
+// to nearly fp32 accuracy on the bf16 matrix cores.
+__device__ __forceinline__ void split8(const floatx4& a, const floatx4& b, bf16x8& hi,
+                                       bf16x8& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = (__bf16)a[i];
+    lo[i] = (__bf16)(a[i] - (float)hi[i]);
+    hi[i + 4] = (__bf16)b[i];
+    lo[i + 4] = (__bf16)(b[i] - (float)hi[i + 4]);
+  }
+}
+
+__device__ __forceinline__ floatx4 fload4(__amdgpu_buffer_rsrc_t r, int e) {
+  return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, e * 4, 0, 0));
+}
+
 // ------------------------------------------------------------------ the kernel
 
 // Per-variant launch shape. A workgroup covers `rows` blocks of 32 query rows of one
@@ -102,7 +122,6 @@ __device__ __forceinline__ void softmax_step(floatx16 (&s)[2], float& m, float& 
 // block, one per softmax map (map 0 on head-dim channels [0, d/2), map 1 on [d/2, d)); both
 // stream the same K/V tiles from LDS and combine their outputs through LDS at the end, so
 // each wave holds one accumulator set, like a full-attention wave with half-width scores.
-// Register budget: two waves per SIMD.
 template <int VAR>
 struct Shape {
   static constexpr int maps = (VAR == kDifferential) ? 2 : 1;
@@ -110,16 +129,19 @@ struct Shape {
   static constexpr int waves = rows * maps;
   static constexpr int threads = waves * kWave;
   static constexpr int bm = 32 * rows;  // query rows per workgroup
-  static constexpr int occupancy = 2;
 };
+// Waves per SIMD the register allocation targets. At d=128 the split K tiles take 104 KiB
+// of LDS, one workgroup per CU: one wave per SIMD for full and sliding (4 waves), two for
+// the differential (8 waves). At d=64 (54 KiB) two workgroups fit.
+template <int D, int VAR>
+constexpr int kOccupancy = (D == 128 && VAR != kDifferential) ? 1 : 2;
 
-template <int D, int VAR, typename Tin>
+template <int D, int VAR>
 __global__ void __attribute__((amdgpu_flat_work_group_size(Shape<VAR>::threads,
                                                            Shape<VAR>::threads),
-                               amdgpu_waves_per_eu(Shape<VAR>::occupancy,
-                                                   Shape<VAR>::occupancy)))
-prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
-               const Tin* __restrict__ vg, Tin* __restrict__ og, int L, int BH, int G,
+                               amdgpu_waves_per_eu(kOccupancy<D, VAR>, kOccupancy<D, VAR>)))
+prefill_kernel(const float* __restrict__ qg, const float* __restrict__ kg,
+               const float* __restrict__ vg, float* __restrict__ og, int L, int BH, int G,
                int nq, int window, float lambda) {
   constexpr bool kDiff = (VAR == kDifferential);
   constexpr bool kSlide = (VAR == kSliding);
@@ -141,16 +163,18 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
   static_assert(KCH % kThreads == 0, "K tile staging");
   typedef __bf16 vcvec __attribute__((ext_vector_type(VC)));
 
-  // LDS: two K / V^T tile buffers (tile kt is computed from buffer kt & 1 while tile kt + 1
-  // is written into the other one); after the key loop the differential reuses the space
-  // to pass map 1's scaled output to map 0.
+  // LDS: two buffers each of the K tile's high parts, its low parts and the V^T tile (tile
+  // kt is computed from buffer kt & 1 while tile kt + 1 is written into the other one);
+  // after the key loop the differential reuses the space to pass map 1's scaled output to
+  // map 0.
   constexpr int kKsElems = BN * KP, kVtElems = D * VP;
-  constexpr int kTileBytes = 2 * (kKsElems + kVtElems) * 2;
+  constexpr int kTileBytes = 2 * (2 * kKsElems + kVtElems) * 2;
   constexpr int kXchBytes = kDiff ? kRows * 64 * (DB * 16) * 4 : 0;
   constexpr int kSmemBytes = kTileBytes > kXchBytes ? kTileBytes : kXchBytes;
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   __bf16* const Ks0 = reinterpret_cast<__bf16*>(smem);
   __bf16* const Vt0 = Ks0 + 2 * kKsElems;
+  __bf16* const Kl0 = Vt0 + 2 * kVtElems;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -167,7 +191,7 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
   const int qi = qw + lr;         // this lane's query row
   const size_t head = (size_t)bh * (size_t)L * D;         // q and out
   const size_t kv_head = (size_t)(bh / G) * (size_t)L * D;  // k and v: G query heads each
-  const int head_bytes = L * D * (int)sizeof(Tin);
+  const int head_bytes = L * D * (int)sizeof(float);
   const __amdgpu_buffer_rsrc_t Qr = make_rsrc(qg + head, head_bytes);
   const __amdgpu_buffer_rsrc_t Kr = make_rsrc(kg + kv_head, head_bytes);
   const __amdgpu_buffer_rsrc_t Vr = make_rsrc(vg + kv_head, head_bytes);
@@ -177,11 +201,14 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
   // First score channel of this wave's map.
   const int ch0 = kDiff ? map * (D / 2) : 0;
 
-  // Q fragments (B operand of S^T = K Q^T): lane holds row qi, channels
-  // ch0 + kk*16 + lg*8 + [0,8). Rows past L read zeros and are never stored.
-  bf16x8 qf[NQ];
+  // Q fragments (B operand of S^T = K Q^T), high and low bf16 parts: lane holds row qi,
+  // channels ch0 + kk*16 + lg*8 + [0,8). Rows past L read zeros and are never stored.
+  bf16x8 qf[NQ], ql[NQ];
 #pragma unroll
-  for (int kk = 0; kk < NQ; ++kk) qf[kk] = bload8<Tin>(Qr, qi * D + ch0 + kk * 16 + lg * 8);
+  for (int kk = 0; kk < NQ; ++kk) {
+    const int e = qi * D + ch0 + kk * 16 + lg * 8;
+    split8(fload4(Qr, e), fload4(Qr, e + 4), qf[kk], ql[kk]);
+  }
   // Wait for Q here, once: otherwise the wait-count insertion cannot prove inside the key
   // loop that Q has arrived, and makes every tile's first score products wait for all
   // vector loads in flight, the next tile's prefetch included.
@@ -206,7 +233,8 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
   float m = -INFINITY, l = 0.0f;
 
   // Register staging of one K/V tile (element offsets within the head; keys past L read 0).
-  bf16x8 kreg[KPT];
+  // K stays fp32 until it is split into LDS; V is rounded to bf16 as it loads.
+  floatx4 kreg[KPT][2];
   vcvec vreg[VPT][4];
   auto fetch = [&](int kt) {
     const int k0 = kt * BN;
@@ -214,7 +242,8 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
     for (int i = 0; i < KPT; ++i) {
       const int idx = tid + i * kThreads;
       const int row = idx / (D / 8), ch = idx % (D / 8);
-      kreg[i] = bload8<Tin>(Kr, (k0 + row) * D + ch * 8);
+      kreg[i][0] = fload4(Kr, (k0 + row) * D + ch * 8);
+      kreg[i][1] = fload4(Kr, (k0 + row) * D + ch * 8 + 4);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -225,21 +254,25 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
         for (int r = 0; r < 4; ++r) {
           const int off = (k0 + a4 * 4 + r) * D + cc * VC;
           if constexpr (VC == 8)
-            vreg[i][r] = bload8<Tin>(Vr, off);
+            vreg[i][r] = bload8<float>(Vr, off);
           else
-            vreg[i][r] = bload4<Tin>(Vr, off);
+            vreg[i][r] = bload4<float>(Vr, off);
         }
       }
     }
   };
   auto stage = [&](int buf) {
     __bf16* const Ks = Ks0 + buf * kKsElems;
+    __bf16* const Kl = Kl0 + buf * kKsElems;
     __bf16* const Vt = Vt0 + buf * kVtElems;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int idx = tid + i * kThreads;
       const int row = idx / (D / 8), ch = idx % (D / 8);
-      *reinterpret_cast<bf16x8*>(&Ks[row * KP + ch * 8]) = kreg[i];
+      bf16x8 hi, lo;
+      split8(kreg[i][0], kreg[i][1], hi, lo);
+      *reinterpret_cast<bf16x8*>(&Ks[row * KP + ch * 8]) = hi;
+      *reinterpret_cast<bf16x8*>(&Kl[row * KP + ch * 8]) = lo;
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -280,19 +313,26 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
       bool full_tile = (k0 + BN - 1 <= qw);
       if (kSlide) full_tile = full_tile && (qw + 31 - k0 < window);
       const __bf16* const Ks = Ks0 + buf * kKsElems;
+      const __bf16* const Kl = Kl0 + buf * kKsElems;
       const __bf16* const Vt = Vt0 + buf * kVtElems;
 
       // ---- scores S^T = K Q^T for 64 keys x 32 queries (two 32x32 blocks) over this
-      // wave's score channels
+      // wave's score channels, from the split operands: Khi Qhi + Khi Qlo + Klo Qhi (the
+      // dropped Klo Qlo term is below 2^-16 of each product)
       floatx16 s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-        const __bf16* krow = &Ks[(kb * 32 + lr) * KP + ch0 + lg * 8];
+        const int koff = (kb * 32 + lr) * KP + ch0 + lg * 8;
 #pragma unroll
-        for (int kk = 0; kk < NQ; ++kk)
-          s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(krow + kk * 16), qf[kk], s[kb]);
+        for (int kk = 0; kk < NQ; ++kk) {
+          const bf16x8 khi = *reinterpret_cast<const bf16x8*>(&Ks[koff + kk * 16]);
+          const bf16x8 klo = *reinterpret_cast<const bf16x8*>(&Kl[koff + kk * 16]);
+          s[kb] = mfma32(khi, qf[kk], s[kb]);
+          s[kb] = mfma32(khi, ql[kk], s[kb]);
+          s[kb] = mfma32(klo, qf[kk], s[kb]);
+        }
       }
       // ---- mask on tiles that cross the diagonal or the window edge
       if (!full_tile) {
@@ -344,7 +384,7 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
   if (qi < L) {
     const float inv = 1.0f / lsum;
     const float* const xch = reinterpret_cast<const float*>(smem) + rb * 64 * (DB * 16);
-    Tin* orow = og + head + (size_t)qi * D;
+    float* orow = og + head + (size_t)qi * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -362,30 +402,30 @@ prefill_kernel(const Tin* __restrict__ qg, const Tin* __restrict__ kg,
 
 // ------------------------------------------------------------------ launch
 
-template <int D, int VAR, typename Tin>
+template <int D, int VAR>
 static hipError_t launch_t(const PrefillLaunch& a, hipStream_t stream) {
   constexpr int BM = Shape<VAR>::bm;
   const int nq = (a.L + BM - 1) / BM;
   const int BH = a.B * a.H;
   const dim3 grid((unsigned)(BH * nq));
-  hipLaunchKernelGGL((prefill_kernel<D, VAR, Tin>), grid, dim3(Shape<VAR>::threads), 0, stream,
-                     static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
-                     static_cast<const Tin*>(a.v), static_cast<Tin*>(a.out), a.L, BH,
+  hipLaunchKernelGGL((prefill_kernel<D, VAR>), grid, dim3(Shape<VAR>::threads), 0, stream,
+                     static_cast<const float*>(a.q), static_cast<const float*>(a.k),
+                     static_cast<const float*>(a.v), static_cast<float*>(a.out), a.L, BH,
                      a.H / a.Hkv, nq, a.window, a.lambda);
   return hipGetLastError();
 }
 
-template <int D, typename Tin>
+template <int D>
 static hipError_t launch_v(const PrefillLaunch& a, hipStream_t stream) {
   switch (a.variant) {
-    case kFull: return launch_t<D, kFull, Tin>(a, stream);
-    case kSliding: return launch_t<D, kSliding, Tin>(a, stream);
-    default: return launch_t<D, kDifferential, Tin>(a, stream);
+    case kFull: return launch_t<D, kFull>(a, stream);
+    case kSliding: return launch_t<D, kSliding>(a, stream);
+    default: return launch_t<D, kDifferential>(a, stream);
   }
 }
 
 hipError_t launch_prefill_regstage(const PrefillLaunch& a, hipStream_t stream) {
-  return a.d == 64 ? launch_v<64, float>(a, stream) : launch_v<128, float>(a, stream);
+  return a.d == 64 ? launch_v<64>(a, stream) : launch_v<128>(a, stream);
 }
 
 

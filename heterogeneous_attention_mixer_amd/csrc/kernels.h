@@ -25,7 +25,7 @@ struct PrefillLaunch {
 
 // Enqueues the layer on `stream`; returns the launch status. bf16 layers run the LDS-DMA
 // kernel (attn_prefill_dma.hip), fp32 layers the register-staged kernel (attn_prefill.hip),
-// which rounds to bf16 as it stages.
+// which splits q and k into bf16 high and low parts and rounds v to bf16 as it stages.
 hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream);
 hipError_t launch_prefill_dma(const PrefillLaunch& a, hipStream_t stream);
 hipError_t launch_prefill_regstage(const PrefillLaunch& a, hipStream_t stream);

@@ -167,7 +167,8 @@ def mixer_prefill(q, k, v, out, variant, window: int = 0, lam: float = 0.0):
 
 def mixer_prefill_f32_async(q, k, v, out, variant, window: int = 0, lam: float = 0.0,
                             stream=None):
-    """One layer on fp32 tensors (rounded to bf16 on load, fp32 result)."""
+    """One layer on fp32 tensors: scores from split (high + low bf16) q and k, v rounded to
+    bf16 on load, fp32 result."""
     import torch
     B, H, L, d = _shape(q, k, v, out, torch.float32)
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_of(q)

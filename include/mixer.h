@@ -98,9 +98,11 @@ int mixer_prefill(const void *q, const void *k, const void *v, void *out,
                   int variant, int window, float lambda, int B, int H, int L, int d);
 
 /*
- * mixer_prefill_f32_async -- the same layer for fp32 inputs and output: each element is
- * rounded to bf16 (nearest-even) as it is loaded, the arithmetic is that of the bf16 entry
- * point, and the fp32 result is stored without rounding. Same arguments and errors as
+ * mixer_prefill_f32_async -- the same layer for fp32 inputs and output. q and k are split
+ * into bf16 high and low parts and the scores are the sum of three products (hi*hi, hi*lo,
+ * lo*hi), so they carry nearly fp32 accuracy; v is rounded to bf16 (nearest-even) as it is
+ * loaded; the rest is the bf16 entry point's arithmetic, and the fp32 result is stored
+ * without rounding. Same arguments and errors as
  * mixer_prefill_async, with float pointers.
  */
 int mixer_prefill_f32_async(const float *q, const float *k, const float *v, float *out,

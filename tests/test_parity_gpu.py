@@ -150,6 +150,20 @@ def test_moving_reference_max_every_row(torch_cuda, oracle_mod, profile, variant
                  f"{profile} keys, {variant} d={d}")
 
 
+@pytest.mark.parametrize("profile", sorted(KEY_PROFILES))
+@pytest.mark.parametrize("variant,W,lam", [("full", 0, 0.0), ("sliding", 200, 0.0),
+                                           ("differential", 0, 0.8)])
+def test_moving_reference_max_fp32_entry(torch_cuda, oracle_mod, profile, variant, W, lam):
+    """The same key profiles through the fp32 entry point (its own kernel, which rounds to
+    bf16 as it stages; the oracle takes the fp32 values)."""
+    L = 500
+    inp = make(980, 1, 2, L, 128, "f32")
+    inp.k[...] = (inp.k * KEY_PROFILES[profile](L)[None, None, :, None]).astype(np.float32)
+    out = run_layer(device_tensors(inp), variant, W, lam)
+    assert_close(to_f64(out), _oracle(oracle_mod, inp, variant, W, lam),
+                 f"fp32 {profile} keys, {variant}")
+
+
 # ------------------------------------------------------------------------ invariants
 
 @pytest.mark.parametrize("variant,W,lam,expect", [("full", 0, 0.0, 1.0),
