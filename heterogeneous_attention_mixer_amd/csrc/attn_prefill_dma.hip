@@ -36,9 +36,10 @@
 //     only when a score beats it by more than 2^8 (probabilities stay below 256), so the
 //     accumulator rescale is rare. Row sums are taken over the bf16-rounded probabilities,
 //     the exact weights of the value product.
-//   * The differential gives each softmax map its own wave (scores on its half of the head
-//     dim, values on all of it); the two waves of a row block meet once, at the end,
-//     through LDS.
+//   * The differential runs its own kernel (prefill_diff_kernel, below): each softmax map
+//     gets its own wave (scores on its half of the head dim, values on all of it), and the
+//     two waves of a row block, which share a SIMD, alternate between a matrix phase and a
+//     vector phase one phase apart; they meet once, at the end, through LDS.
 //   * Work order: heaviest query tiles first; all tiles of a head on one XCD when B*H is a
 //     multiple of 8.
 #include <hip/hip_runtime.h>
@@ -56,18 +57,12 @@ namespace dma {
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-// Launch shape: 4 blocks of 32 query rows per workgroup; the differential adds a second
-// wave per row block for its second map. Register budget: two waves per SIMD, so full and
-// sliding run two workgroups per CU and the differential one. (Two row blocks for the
-// differential, i.e. two 4-wave workgroups per CU, measured slower: twice the K/V bytes
-// moved per flop.)
-template <int VAR>
+// Launch shape of the full and sliding kernel: 4 waves of 32 query rows per workgroup.
+// Register budget: two waves per SIMD, i.e. two independent workgroups per CU.
 struct DShape {
-  static constexpr int maps = (VAR == kDifferential) ? 2 : 1;
-  static constexpr int rows = 4;
-  static constexpr int waves = rows * maps;
+  static constexpr int waves = 4;
   static constexpr int threads = waves * kWave;
-  static constexpr int bm = 32 * rows;
+  static constexpr int bm = 32 * waves;
 };
 
 // Chunk swizzle of a tile row: the 16-byte chunk c of row r is stored at chunk c ^ swz(r).
@@ -141,19 +136,16 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 }
 
 template <int D, int VAR>
-__global__ void __attribute__((amdgpu_flat_work_group_size(DShape<VAR>::threads,
-                                                           DShape<VAR>::threads),
+__global__ void __attribute__((amdgpu_flat_work_group_size(DShape::threads, DShape::threads),
                                amdgpu_waves_per_eu(2, 2)))
 prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
                    const __bf16* __restrict__ vg, __bf16* __restrict__ og, int L, int BH,
-                   int G, int nq, int window, float lambda) {
-  constexpr bool kDiff = (VAR == kDifferential);
+                   int G, int nq, int window) {
+  static_assert(VAR == kFull || VAR == kSliding, "the differential has its own kernel");
   constexpr bool kSlide = (VAR == kSliding);
-  constexpr int kWaves = DShape<VAR>::waves;
-  constexpr int kRows = DShape<VAR>::rows;
-  constexpr int BM = DShape<VAR>::bm;
-  constexpr int KSTEPS = D / 16;                  // MFMA steps over the head dim
-  constexpr int NQ = KSTEPS / DShape<VAR>::maps;  // ... over one map's score channels
+  constexpr int kWaves = DShape::waves;
+  constexpr int BM = DShape::bm;
+  constexpr int NQ = D / 16;                      // MFMA steps over the head dim
   constexpr int DB = D / 32;                      // 32-channel blocks of O^T
   constexpr int ROWB = D * 2;                     // bytes per K/V row
   constexpr int TILEB = BN * ROWB;                // bytes per K/V tile
@@ -162,10 +154,8 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   constexpr int CPR = D / 8;                      // 16-byte chunks per row
   static_assert(NI % kWaves == 0, "tile loads must split evenly over the waves");
 
-  // LDS: K buffers 0, 1 then V buffers 0, 1; reused after the key loop by the differential.
-  constexpr int kXchBytes = kDiff ? kRows * 64 * (DB * 16) * 4 : 0;
-  constexpr int kSmem = (4 * TILEB > kXchBytes) ? 4 * TILEB : kXchBytes;
-  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
+  // LDS: K buffers 0, 1 then V buffers 0, 1.
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];
   lds_char* const lds = (lds_char*)(smem);
   const unsigned lds_addr = (unsigned)(uintptr_t)lds;  // LDS byte address of smem
 
@@ -173,8 +163,7 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // the same value, in an SGPR
-  const int rb = wave % kRows;  // row block of this wave
-  const int map = wave / kRows;  // softmax map of this wave (differential)
+  const int rb = wave;  // row block of this wave
   const int lr = lane & 31;
   const int lg = lane >> 5;
 
@@ -190,14 +179,13 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   const unsigned long long Kbase = reinterpret_cast<unsigned long long>(kg + kv_head);
   const unsigned long long Vbase = reinterpret_cast<unsigned long long>(vg + kv_head);
 
-  const float c = kLog2e / __builtin_sqrtf(kDiff ? (float)(D / 2) : (float)D);
+  const float c = kLog2e / __builtin_sqrtf((float)D);
   const float gap = kRescaleLog2Gap / c;
-  const int ch0 = kDiff ? map * (D / 2) : 0;  // first score channel of this wave's map
 
-  // Q fragments: lane holds row qi, channels ch0 + kk*16 + lg*8 + [0, 8).
+  // Q fragments: lane holds row qi, channels kk*16 + lg*8 + [0, 8).
   bf16x8 qf[NQ];
 #pragma unroll
-  for (int kk = 0; kk < NQ; ++kk) qf[kk] = bload8<__bf16>(Qr, qi * D + ch0 + kk * 16 + lg * 8);
+  for (int kk = 0; kk < NQ; ++kk) qf[kk] = bload8<__bf16>(Qr, qi * D + kk * 16 + lg * 8);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
   // ---- per-lane address parts, fixed for the whole kernel
@@ -212,12 +200,11 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
     ld_off[t] = r * ROWB + (((lane % CPR) ^ swz<D>(r)) << 4);
   }
   // K operand reads: row kb*32 + lr (the swizzle depends on the row mod 16 only), chunk
-  // ch0/8 + 2*kk + lg.
+  // 2*kk + lg.
   const int k_sw = swz<D>(lr);
   int k_off[NQ];
 #pragma unroll
-  for (int kk = 0; kk < NQ; ++kk)
-    k_off[kk] = lr * ROWB + (((ch0 / 8 + 2 * kk + lg) ^ k_sw) << 4);
+  for (int kk = 0; kk < NQ; ++kk) k_off[kk] = lr * ROWB + (((2 * kk + lg) ^ k_sw) << 4);
   // V^T operand reads (transposed, 8 bytes per lane): for the 16-key half h of key block kb
   // and read rr, lane (group g = lane/16, s = lane%16) reads key row
   // kb*32 + 16h + 8rr + 4*lg + s/4, channels db*32 + 16*(g%2) + 4*(s%4) + [0, 4).
@@ -478,12 +465,292 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   else
     pv(std::integral_constant<int, 2 * TILEB>{}, pr[0]);
 
-  // ---- epilogue: out = O / l; differential: O1 / l1 - lambda * O2 / l2 with map 1's term
-  // passed to map 0 through LDS. Element (db, r) of a lane is channel
+  // ---- epilogue: out = O / l. Element (db, r) of a lane is channel
   // db*32 + 8*(r/4) + 4*lg + r%4 of query qi.
   const float lsum = xhalf_sum(l);
-  if constexpr (kDiff) {
-    __syncthreads();  // every wave is done reading the V tiles
+  if (qi < L) {
+    const float inv = 1.0f / lsum;
+    __bf16* orow = og + head + (size_t)qi * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        store4(orow + db * 32 + 8 * r4 + 4 * lg, o[db][r4 * 4] * inv, o[db][r4 * 4 + 1] * inv,
+               o[db][r4 * 4 + 2] * inv, o[db][r4 * 4 + 3] * inv);
+  }
+}
+
+// ---------------------------------------------------------------- the differential kernel
+//
+// Eight waves, two per SIMD: row block rb's two maps are waves rb (map 0) and rb + 4
+// (map 1), and they sit on the same SIMD. Each wave has one map's softmax over half of the
+// head dim and the value product over all of it; the two maps of a row block meet once, at
+// the end, through LDS. The map-1 waves run one phase behind the map-0 waves. Per key tile
+// k a wave runs an M phase (matrix work only: S[k] = K[k] Q^T, then O += V[k-1] P[k-1]) and
+// a V phase (vector work only: row max, reference move and O rescale, the exponentials of
+// S[k] into P[k], and the loads of later tiles). So on every SIMD one wave feeds the matrix
+// core while its partner does the softmax, and a barrier ends every phase. The M phase runs
+// at raised wave priority, so the arbiter favours the matrix instructions. Within a wave the
+// phases strictly alternate, so one set of score and probability registers is enough.
+// K[k] and V[k-1] (the pair of tile k) live in LDS buffer pair k mod 4; the loads of pair
+// k+3 are issued in the V phase of tile k.
+struct DiffShape {
+  static constexpr int maps = 2;
+  static constexpr int rows = 4;  // 32-row blocks
+  static constexpr int waves = rows * maps;
+  static constexpr int threads = waves * kWave;
+  static constexpr int bm = 32 * rows;
+};
+
+template <int D>
+__global__ void __attribute__((amdgpu_flat_work_group_size(DiffShape::threads,
+                                                           DiffShape::threads),
+                               amdgpu_waves_per_eu(2, 2)))
+prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
+                    const __bf16* __restrict__ vg, __bf16* __restrict__ og, int L, int BH,
+                    int G, int nq, float lambda) {
+  constexpr int kWaves = DiffShape::waves;
+  constexpr int kRows = DiffShape::rows;
+  constexpr int BM = DiffShape::bm;
+  constexpr int NQ = D / 32;  // MFMA steps over one map's d/2 score channels
+  constexpr int DB = D / 32;
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = BN * ROWB;
+  constexpr int NI = TILEB / 1024;
+  constexpr int NIW = NI / kWaves;
+  constexpr int CPR = D / 8;
+  static_assert(NI % kWaves == 0, "tile loads must split evenly over the waves");
+  // LDS: K buffers 0..3, then V buffers 0..3; reused after the key loop to pass map 1's
+  // output to map 0.
+  constexpr int kXchBytes = kRows * 64 * (DB * 16) * 4;
+  constexpr int kSmem = (8 * TILEB > kXchBytes) ? 8 * TILEB : kXchBytes;
+  // At the end of an M phase every load but those issued in the wave's last V phase is in.
+  constexpr int kWaitOlder = 0x0F70 | (2 * NIW);
+  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
+  lds_char* const lds = (lds_char*)(smem);
+  const unsigned lds_addr = (unsigned)(uintptr_t)lds;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int grp = wave_s >> 2;     // phase group (waves w and w + 4 share a SIMD)
+  const int rb = wave % kRows;     // row block of this wave
+  const int map = wave / kRows;    // softmax map (differential)
+  const int lr = lane & 31;
+  const int lg = lane >> 5;
+
+  int bh, qt;
+  map_unit(blockIdx.x, BH, nq, &bh, &qt);
+  const int q0 = qt * BM;
+  const int qw = q0 + rb * 32;
+  const int qi = qw + lr;
+  const size_t head = (size_t)bh * (size_t)L * D;
+  const size_t kv_head = (size_t)(bh / G) * (size_t)L * D;
+  const int head_bytes = L * ROWB;
+  const __amdgpu_buffer_rsrc_t Qr = make_rsrc(qg + head, head_bytes);
+  const unsigned long long Kbase = reinterpret_cast<unsigned long long>(kg + kv_head);
+  const unsigned long long Vbase = reinterpret_cast<unsigned long long>(vg + kv_head);
+  const float c = kLog2e / __builtin_sqrtf((float)(D / 2));
+  const float gap = kRescaleLog2Gap / c;
+  const int ch0 = map * (D / 2);  // first score channel of this wave's map
+
+  bf16x8 qf[NQ];
+#pragma unroll
+  for (int kk = 0; kk < NQ; ++kk) qf[kk] = bload8<__bf16>(Qr, qi * D + ch0 + kk * 16 + lg * 8);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+
+  // Per-lane address parts (the same chunk swizzle and read patterns as the pipelined
+  // kernel; V offsets carry the V region's base).
+  int ld_off[NIW];
+#pragma unroll
+  for (int t = 0; t < NIW; ++t) {
+    const int i = wave + t * kWaves;
+    const int r = i * (1024 / ROWB) + lane / CPR;
+    ld_off[t] = r * ROWB + (((lane % CPR) ^ swz<D>(r)) << 4);
+  }
+  const int k_sw = swz<D>(lr);
+  int k_off[NQ];
+#pragma unroll
+  for (int kk = 0; kk < NQ; ++kk)
+    k_off[kk] = lr * ROWB + (((ch0 / 8 + 2 * kk + lg) ^ k_sw) << 4);
+  const int vs = lane & 15, vdh = (lane >> 4) & 1;
+  int v_off[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int r = 8 * rr + 4 * lg + (vs >> 2);
+      const int chunk = 4 * db + 2 * vdh + ((vs & 3) >> 1);
+      v_off[db][rr] = 4 * TILEB + r * ROWB + ((chunk ^ swz<D>(r)) << 4) + (vs & 1) * 8;
+    }
+
+  const int q_last = min(q0 + BM, L) - 1;
+  const int lo = 0;
+  const int hi = q_last / BN;
+
+  auto load_tile = [&](bool v, int dst, int j) {
+    const u32x4 r = rsrc_words((v ? Vbase : Kbase) + (unsigned long long)j * TILEB,
+                               head_bytes - j * TILEB);
+#pragma unroll
+    for (int t = 0; t < NIW; ++t)
+      lds_load16(r, (unsigned)(lds_addr + dst + (wave_s + t * kWaves) * 1024), ld_off[t]);
+  };
+  // Does every row of the wave see every key of tile j?
+  auto full_tile = [&](int j) { return j * BN + BN - 1 <= qw; };
+
+  floatx16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+  float m = -INFINITY, l = 0.0f;
+  floatx16 s[2];
+  bf16x8 p[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[kb][h][e] = (__bf16)0.0f;
+
+  // M phase of tile k (pair buffer `pb`): S = K[k] Q^T; O += V[k-1] P.
+  auto m_phase = [&](int pb) {
+    const int kbase = pb * TILEB;
+    int ka[NQ], va[DB][2];
+#pragma unroll
+    for (int kk = 0; kk < NQ; ++kk) ka[kk] = k_off[kk] + kbase;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) va[db][rr] = v_off[db][rr] + kbase;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < NQ; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+            lds + ka[kk] + kb * 32 * ROWB);
+        s[kb] = mfma32(a, qf[kk], s[kb]);
+      }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int roff = (kb * 32 + 16 * h) * ROWB;
+          const shortx4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              reinterpret_cast<__attribute__((address_space(3))) shortx4*>(
+                  lds + va[db][0] + roff));
+          const shortx4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              reinterpret_cast<__attribute__((address_space(3))) shortx4*>(
+                  lds + va[db][1] + roff));
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[db] = mfma32(a, p[kb][h], o[db]);
+        }
+    // Operand reads a few instructions ahead of the matrix instructions that use them.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < (DB * 4 + 2 * NQ) / 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  // V phase of tile k: loads of pair k+3, then the softmax step of S into P.
+  auto v_phase = [&](int k) {
+    const int nb = ((k + 3 - lo) & 3) * TILEB;
+    load_tile(false, nb, k + 3);
+    load_tile(true, 4 * TILEB + nb, k + 2);
+    if (!full_tile(k)) {
+      // Element (kb, r) holds key k*BN + cc + 4*lg with cc a compile-time constant: visible
+      // when cc <= qi - k*BN - 4*lg.
+      const int t = qi - k * BN - 4 * lg;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + (r & 3) > t) s[kb][r] = -INFINITY;
+    }
+    float t0 = vmax3(s[0][0], s[0][1], s[0][2]);
+    float t1 = vmax3(s[1][0], s[1][1], s[1][2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) {
+      t0 = vmax3(t0, s[0][r], s[0][r + 1]);
+      t1 = vmax3(t1, s[1][r], s[1][r + 1]);
+    }
+    const float tmax = xhalf_max(vmax3(vmax3(t0, s[0][15], t1), s[1][15], s[1][15]));
+    if (__any(tmax > m + gap)) {
+      const float m_new = __builtin_fmaxf(m, tmax);
+      const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2((m - m_new) * c);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      m = m_new;
+    }
+    const float mc = (m == -INFINITY) ? 0.0f : m * c;
+    bf16x2 ones;
+    ones[0] = (__bf16)1.0f;
+    ones[1] = (__bf16)1.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          bf16x2 q2;
+          q2[0] = (__bf16)fast_exp2(__builtin_fmaf(s[kb][h * 8 + e], c, -mc));
+          q2[1] = (__bf16)fast_exp2(__builtin_fmaf(s[kb][h * 8 + e + 1], c, -mc));
+          p[kb][h][e] = q2[0];
+          p[kb][h][e + 1] = q2[1];
+          l = __builtin_amdgcn_fdot2_f32_bf16(q2, ones, l, false);
+        }
+  };
+
+  // ---- prologue: pair lo = (K[lo], zeros), pair lo+1 = (K[lo+1], V[lo]),
+  // pair lo+2 = (K[lo+2], V[lo+1]).
+  {
+    const floatx4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+    floatx4* const vz = reinterpret_cast<floatx4*>(smem + 4 * TILEB);
+#pragma unroll
+    for (int i = tid; i < TILEB / 16; i += kWaves * kWave) vz[i] = z;
+  }
+  load_tile(false, 0 * TILEB, lo);
+  load_tile(false, 1 * TILEB, lo + 1);
+  load_tile(true, 5 * TILEB, lo);
+  load_tile(false, 2 * TILEB, lo + 2);
+  load_tile(true, 6 * TILEB, lo + 1);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+
+  // ---- key loop: group 1 runs one phase behind group 0; both run the same number of
+  // barriers. The last M phase (tile hi+1) only adds V[hi] P[hi]; its scores are discarded.
+  if (grp == 1) __syncthreads();
+  for (int k = lo; k <= hi + 1; ++k) {
+    __builtin_amdgcn_s_setprio(1);
+    m_phase((k - lo) & 3);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_waitcnt(kWaitOlder);
+    __syncthreads();
+    if (k <= hi) v_phase(k);
+    __syncthreads();
+  }
+  if (grp == 0) __syncthreads();
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+
+  // ---- epilogue: out = O1 / l1 - lambda * O2 / l2, map 1's term passed to map 0 through
+  // LDS. Element (db, r) of a lane is channel db*32 + 8*(r/4) + 4*lg + r%4 of query qi.
+  const float lsum = xhalf_sum(l);
+  __syncthreads();  // every wave is done reading the tiles
+  {
     float* const xch = reinterpret_cast<float*>(smem) + rb * 64 * (DB * 16);
     if (map == 1) {
       const float sc = lambda / lsum;
@@ -492,9 +759,9 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
 #pragma unroll
         for (int r = 0; r < 16; ++r) xch[(db * 16 + r) * 64 + lane] = o[db][r] * sc;
     }
-    __syncthreads();
-    if (map == 1) return;
   }
+  __syncthreads();
+  if (map == 1) return;
   if (qi < L) {
     const float inv = 1.0f / lsum;
     const float* const xch = reinterpret_cast<const float*>(smem) + rb * 64 * (DB * 16);
@@ -507,23 +774,36 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           x[e] = o[db][r4 * 4 + e] * inv;
-          if constexpr (kDiff) x[e] -= xch[(db * 16 + r4 * 4 + e) * 64 + lane];
+          x[e] -= xch[(db * 16 + r4 * 4 + e) * 64 + lane];
         }
         store4(orow + db * 32 + 8 * r4 + 4 * lg, x[0], x[1], x[2], x[3]);
       }
   }
 }
 
+
+
 template <int D, int VAR>
 hipError_t launch_dma_t(const PrefillLaunch& a, hipStream_t stream) {
-  constexpr int BM = DShape<VAR>::bm;
+  constexpr int BM = DShape::bm;
   const int nq = (a.L + BM - 1) / BM;
   const int BH = a.B * a.H;
   hipLaunchKernelGGL((prefill_dma_kernel<D, VAR>), dim3((unsigned)(BH * nq)),
-                     dim3(DShape<VAR>::threads), 0, stream, static_cast<const __bf16*>(a.q),
+                     dim3(DShape::threads), 0, stream, static_cast<const __bf16*>(a.q),
                      static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
-                     static_cast<__bf16*>(a.out), a.L, BH, a.H / a.Hkv, nq, a.window,
-                     a.lambda);
+                     static_cast<__bf16*>(a.out), a.L, BH, a.H / a.Hkv, nq, a.window);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_diff(const PrefillLaunch& a, hipStream_t stream) {
+  constexpr int BM = DiffShape::bm;
+  const int nq = (a.L + BM - 1) / BM;
+  const int BH = a.B * a.H;
+  hipLaunchKernelGGL((prefill_diff_kernel<D>), dim3((unsigned)(BH * nq)),
+                     dim3(DiffShape::threads), 0, stream, static_cast<const __bf16*>(a.q),
+                     static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
+                     static_cast<__bf16*>(a.out), a.L, BH, a.H / a.Hkv, nq, a.lambda);
   return hipGetLastError();
 }
 
@@ -532,7 +812,7 @@ hipError_t launch_dma_v(const PrefillLaunch& a, hipStream_t stream) {
   switch (a.variant) {
     case kFull: return launch_dma_t<D, kFull>(a, stream);
     case kSliding: return launch_dma_t<D, kSliding>(a, stream);
-    default: return launch_dma_t<D, kDifferential>(a, stream);
+    default: return launch_diff<D>(a, stream);
   }
 }
 
