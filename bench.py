@@ -57,7 +57,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 # Sources of the bf16 kernel the bench times (a traffic summary is valid only for them).
 KERNEL_SOURCES = [os.path.join(ROOT, "heterogeneous_attention_mixer_amd", "csrc", f)
                   for f in ("attn_prefill_dma.hip", "device_common.h", "kernels.h")]
-KERNEL_NAME = "prefill_dma_kernel"
+# The d=128 bf16 kernel of each variant: its name as reported, and a substring of its
+# mangled symbol in profiler output.
+KERNELS = {"full": ("prefill_dma_kernel<128, full>", "prefill_dma_kernelILi128ELi0E"),
+           "sliding": ("prefill_dma_kernel<128, sliding>", "prefill_dma_kernelILi128ELi1E"),
+           "differential": ("prefill_diff_kernel<128>", "prefill_diff_kernelILi128EE")}
 
 
 def visible_pairs(variant: str, L: int, window: int) -> int:
@@ -116,8 +120,6 @@ def read_traffic(variant: str):
 
 
 COPY_BYTES = 256 * 1024 * 1024  # the --copy-calibration copy: reads and writes this much
-KERNEL_VARIANT_TAGS = {"ILi128ELi0E": "full", "ILi128ELi1E": "sliding",
-                       "ILi128ELi2E": "differential"}
 
 
 def write_traffic(fetch_csv: str, write_csv: str, command: str) -> str:
@@ -134,8 +136,7 @@ def write_traffic(fetch_csv: str, write_csv: str, command: str) -> str:
                 if r["Counter_Name"] != counter:
                     continue
                 name = r["Kernel_Name"]
-                key = next((v for k, v in KERNEL_VARIANT_TAGS.items()
-                            if KERNEL_NAME in name and k in name),
+                key = next((v for v, (_, tag) in KERNELS.items() if tag in name),
                            "copy" if "copyBuffer" in name else None)
                 if key:
                     out.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
@@ -147,7 +148,7 @@ def write_traffic(fetch_csv: str, write_csv: str, command: str) -> str:
         raise SystemExit("no copy-kernel calibration in the counter files")
     fscale = COPY_BYTES / fetch["copy"]
     wscale = COPY_BYTES / write["copy"]
-    lines = [f"# HBM bytes per launch of {KERNEL_NAME}<128, variant> at B=1 H=16 L=8192",
+    lines = ["# HBM bytes per launch of the d=128 bf16 kernel of each variant at B=1 H=16 L=8192",
              "# (Latin stack workload), from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE,",
              "# each scaled by what it reads for a plain 256 MiB device copy.",
              f"# command: {command}",
@@ -359,7 +360,7 @@ def main(argv=None) -> int:
     achieved = dom["useful_tflops"]
     roofline = {
         "bound": "mfma",
-        "kernel": f"{KERNEL_NAME}<128, {dominant}> (bf16)",
+        "kernel": f"{KERNELS[dominant][0]} (bf16)",
         "achieved": achieved,
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
