@@ -715,8 +715,8 @@ prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg
         }
   };
 
-  // ---- prologue: pair lo = (K[lo], zeros), pair lo+1 = (K[lo+1], V[lo]),
-  // pair lo+2 = (K[lo+2], V[lo+1]).
+  // ---- prologue (lo is tile 0): pair 0 = (K[0], zeros), pair 1 = (K[1], V[0]),
+  // pair 2 = (K[2], V[1]).
   {
     const floatx4 z = {0.0f, 0.0f, 0.0f, 0.0f};
     floatx4* const vz = reinterpret_cast<floatx4*>(smem + 4 * TILEB);
