@@ -39,7 +39,10 @@
 //   * The differential runs its own kernel (prefill_diff_kernel, below): each softmax map
 //     gets its own wave (scores on its half of the head dim, values on all of it), and the
 //     two waves of a row block, which share a SIMD, alternate between a matrix phase and a
-//     vector phase one phase apart; they meet once, at the end, through LDS.
+//     vector phase one phase apart; they meet once, at the end, through LDS. Its vector
+//     phase takes the exponentials against the current reference and leaves the row max to
+//     a rare path at the start of the next matrix phase, taken only while a row has no
+//     reference or when the lane's tile sum exceeds 2^8.
 //   * Work order: heaviest query tiles first; all tiles of a head on one XCD when B*H is a
 //     multiple of 8.
 #include <hip/hip_runtime.h>
@@ -487,8 +490,11 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
 // head dim and the value product over all of it; the two maps of a row block meet once, at
 // the end, through LDS. The map-1 waves run one phase behind the map-0 waves. Per key tile
 // k a wave runs an M phase (matrix work only: S[k] = K[k] Q^T, then O += V[k-1] P[k-1]) and
-// a V phase (vector work only: row max, reference move and O rescale, the exponentials of
-// S[k] into P[k], and the loads of later tiles). So on every SIMD one wave feeds the matrix
+// a V phase (vector work only: the exponentials of S[k] into P[k] against the current
+// reference, their sum in four independent partial sums, and the loads of later tiles). The
+// reference test for tile k (no reference yet, or a lane's tile sum above 2^8: then the row
+// max, the move with l and O, and the exponentials again) runs at the start of the M phase
+// of tile k+1, before S is overwritten; it is rare. So on every SIMD one wave feeds the matrix
 // core while its partner does the softmax, and a barrier ends every phase. The M phase runs
 // at raised wave priority, so the arbiter favours the matrix instructions. Within a wave the
 // phases strictly alternate, so one set of score and probability registers is enough.
@@ -552,7 +558,6 @@ prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg
   const unsigned long long Kbase = reinterpret_cast<unsigned long long>(kg + kv_head);
   const unsigned long long Vbase = reinterpret_cast<unsigned long long>(vg + kv_head);
   const float c = kLog2e / __builtin_sqrtf((float)(D / 2));
-  const float gap = kRescaleLog2Gap / c;
   const int ch0 = map * (D / 2);  // first score channel of this wave's map
 
   bf16x8 qf[NQ];
@@ -605,6 +610,7 @@ prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   float m = -INFINITY, l = 0.0f;
+  float lt = 0.0f;  // this lane's sum of the last tile's probabilities, not yet in l
   floatx16 s[2];
   bf16x8 p[2][2];
 #pragma unroll
@@ -614,6 +620,58 @@ prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg
 #pragma unroll
       for (int e = 0; e < 8; ++e) p[kb][h][e] = (__bf16)0.0f;
 
+  // Probabilities exp2(c (s - m)) of the tile against the current reference, rounded to
+  // bf16 into p; their sum into lt, over four independent partial sums (one per 16-key
+  // group), so that no 16-long chain of dependent additions sits in the V phase.
+  auto take_exps = [&]() {
+    const float mc = (m == -INFINITY) ? 0.0f : m * c;
+    bf16x2 ones;
+    ones[0] = (__bf16)1.0f;
+    ones[1] = (__bf16)1.0f;
+    float ls[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          bf16x2 q2;
+          q2[0] = (__bf16)fast_exp2(__builtin_fmaf(s[kb][h * 8 + e], c, -mc));
+          q2[1] = (__bf16)fast_exp2(__builtin_fmaf(s[kb][h * 8 + e + 1], c, -mc));
+          p[kb][h][e] = q2[0];
+          p[kb][h][e + 1] = q2[1];
+          ls[kb][h] = __builtin_amdgcn_fdot2_f32_bf16(q2, ones, ls[kb][h], false);
+        }
+    lt = (ls[0][0] + ls[0][1]) + (ls[1][0] + ls[1][1]);
+  };
+  // Reference test for the tile whose probabilities the V phase just took (S still holds
+  // its masked scores). While a row has no reference yet, or when a lane's tile sum says a
+  // probability may exceed 2^gap, the row max moves the reference, l and O follow (O holds
+  // the tiles before this one), and the probabilities are taken again. Then l takes lt.
+  auto settle = [&]() {
+    if (__any((lt > kTileSumBound) | (m == -INFINITY))) {
+      float t0 = vmax3(s[0][0], s[0][1], s[0][2]);
+      float t1 = vmax3(s[1][0], s[1][1], s[1][2]);
+#pragma unroll
+      for (int r = 3; r < 15; r += 2) {
+        t0 = vmax3(t0, s[0][r], s[0][r + 1]);
+        t1 = vmax3(t1, s[1][r], s[1][r + 1]);
+      }
+      const float tmax = xhalf_max(vmax3(vmax3(t0, s[0][15], t1), s[1][15], s[1][15]));
+      const float m_new = __builtin_fmaxf(m, tmax);
+      if (m_new != m) {
+        const float alpha = (m == -INFINITY) ? 0.0f : fast_exp2((m - m_new) * c);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        m = m_new;
+        take_exps();
+      }
+    }
+    l += lt;
+  };
   // M phase of tile k (pair buffer `pb`): S = K[k] Q^T; O += V[k-1] P.
   auto m_phase = [&](int pb) {
     const int kbase = pb * TILEB;
@@ -663,7 +721,8 @@ prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
-  // V phase of tile k: loads of pair k+3, then the softmax step of S into P.
+  // V phase of tile k: loads of pair k+3, then the probabilities of S (masked on tiles
+  // that cross the diagonal) against the current reference.
   auto v_phase = [&](int k) {
     const int nb = ((k + 3 - lo) & 3) * TILEB;
     load_tile(false, nb, k + 3);
@@ -678,41 +737,9 @@ prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg
         for (int r = 0; r < 16; ++r)
           if (kb * 32 + 8 * (r >> 2) + (r & 3) > t) s[kb][r] = -INFINITY;
     }
-    float t0 = vmax3(s[0][0], s[0][1], s[0][2]);
-    float t1 = vmax3(s[1][0], s[1][1], s[1][2]);
-#pragma unroll
-    for (int r = 3; r < 15; r += 2) {
-      t0 = vmax3(t0, s[0][r], s[0][r + 1]);
-      t1 = vmax3(t1, s[1][r], s[1][r + 1]);
-    }
-    const float tmax = xhalf_max(vmax3(vmax3(t0, s[0][15], t1), s[1][15], s[1][15]));
-    if (__any(tmax > m + gap)) {
-      const float m_new = __builtin_fmaxf(m, tmax);
-      const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2((m - m_new) * c);
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      m = m_new;
-    }
-    const float mc = (m == -INFINITY) ? 0.0f : m * c;
-    bf16x2 ones;
-    ones[0] = (__bf16)1.0f;
-    ones[1] = (__bf16)1.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          bf16x2 q2;
-          q2[0] = (__bf16)fast_exp2(__builtin_fmaf(s[kb][h * 8 + e], c, -mc));
-          q2[1] = (__bf16)fast_exp2(__builtin_fmaf(s[kb][h * 8 + e + 1], c, -mc));
-          p[kb][h][e] = q2[0];
-          p[kb][h][e + 1] = q2[1];
-          l = __builtin_amdgcn_fdot2_f32_bf16(q2, ones, l, false);
-        }
+    take_exps();
+    // lt is read only at the start of the next M phase: keep its sums in this phase.
+    asm volatile("" : "+v"(lt));
   };
 
   // ---- prologue (lo is tile 0): pair 0 = (K[0], zeros), pair 1 = (K[1], V[0]),
@@ -735,6 +762,7 @@ prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg
   // barriers. The last M phase (tile hi+1) only adds V[hi] P[hi]; its scores are discarded.
   if (grp == 1) __syncthreads();
   for (int k = lo; k <= hi + 1; ++k) {
+    if (k > lo) settle();  // tile k-1
     __builtin_amdgcn_s_setprio(1);
     m_phase((k - lo) & 3);
     __builtin_amdgcn_s_setprio(0);
