@@ -374,17 +374,29 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
 #pragma unroll
         for (int e = 0; e < 8; ++e) pr[t][kb][h][e] = (__bf16)0.0f;
   load_tile(false, (lo & 1) * TILEB, lo);
-  load_tile(false, ((lo + 1) & 1) * TILEB, lo + 1);
+  if (lo + 1 <= hi) load_tile(false, ((lo + 1) & 1) * TILEB, lo + 1);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
+  // The first tile's scores, unless no row of this wave sees any of its keys (a wave below
+  // the window of the workgroup's first rows): then zeros stand in, and the mask of the
+  // first iteration turns every one of them into -inf.
+  const bool see_lo = kSlide ? (lo * BN + BN - 1 >= q0 + wave_s * 32 - window + 1) : true;
   float tmax_n;  // row max of the scores of the next tile (unmasked)
-  if (lo & 1) {
-    qk_into(std::integral_constant<int, TILEB>{}, sc[1]);
-    tmax_n = row_max(sc[1]);
-  } else {
-    qk_into(std::integral_constant<int, 0>{}, sc[0]);
-    tmax_n = row_max(sc[0]);
-  }
+  auto first_scores = [&](auto koff_c, floatx16(&d)[2]) {
+    if (see_lo) {
+      qk_into(koff_c, d);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) d[kb][r] = 0.0f;
+    }
+    tmax_n = row_max(d);
+  };
+  if (lo & 1)
+    first_scores(std::integral_constant<int, TILEB>{}, sc[1]);
+  else
+    first_scores(std::integral_constant<int, 0>{}, sc[0]);
   __syncthreads();
 
   // ---- key loop. Every wave runs the same sequence on every tile of the workgroup's
@@ -393,14 +405,15 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   // per SIMD.
   float alpha_p = 1.0f;  // pending rescale of O, decided on the previous tile
   bool moved_p = false;
-  // One iteration on tile j, with PAR = j & 1.
-  auto iter = [&](auto par_c, int j) {
+  // One iteration on tile j, with PAR = j & 1; LAST marks tile hi, whose iteration has no
+  // next tile to score.
+  auto iter = [&](auto par_c, auto last_c, int j) {
     constexpr int PAR = decltype(par_c)::value;
+    constexpr bool LAST = decltype(last_c)::value;
     // Loads for the next iteration, issued first: K[j+2] into K's buffer PAR (K[j] was read
-    // during iteration j-1) and V[j] into V's buffer PAR (V[j-2] was read during j-1). On
-    // the last tiles the K load falls outside the workgroup's range: it reads zeros or keys
-    // nobody uses, into a buffer that is not read for a real tile again.
-    load_tile(false, PAR * TILEB, j + 2);
+    // during iteration j-1), while tile j+2 is in the workgroup's range, and V[j] into V's
+    // buffer PAR (V[j-2] was read during j-1).
+    if (!LAST && j + 2 <= hi) load_tile(false, PAR * TILEB, j + 2);
     load_tile(true, (2 + PAR) * TILEB, j);
     // Rescale decided on tile j-1: O holds tiles up to j-2 here, and the value product of
     // tile j-1 below is already on tile j-1's reference.
@@ -421,18 +434,19 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
       l *= alpha;
       m = m_new;
     }
-    // One straight block: S[j+1] = K[j+1] Q^T first, then O += V[j-1] P[j-1]; beside
-    // them the exponentials of tile j and, once S[j+1] is in, its row max (on the last
-    // tile the scores of tile hi+1 come from a stale buffer and are discarded). The group
-    // barriers fix the issue order so that vector work sits between the matrix
-    // instructions: a wave issues in order, and an MFMA waiting for the busy matrix pipe
-    // holds up everything behind it.
-    qk_into(std::integral_constant<int, (1 - PAR) * TILEB>{}, sc[1 - PAR]);
+    // One straight block: S[j+1] = K[j+1] Q^T first (not on the last tile), then
+    // O += V[j-1] P[j-1]; beside them the exponentials of tile j and, once S[j+1] is in,
+    // its row max. The group barriers fix the issue order so that vector work sits between
+    // the matrix instructions: a wave issues in order, and an MFMA waiting for the busy
+    // matrix pipe holds up everything behind it.
+    if constexpr (!LAST) qk_into(std::integral_constant<int, (1 - PAR) * TILEB>{}, sc[1 - PAR]);
     pv(std::integral_constant<int, (3 - PAR) * TILEB>{}, pr[1 - PAR]);
     exps(sc[PAR], pr[PAR]);
-    tmax_n = row_max(sc[1 - PAR]);
-    constexpr int kMfma = DB * 4 + 2 * NQ;  // matrix instructions in the block
-    constexpr int kValu = 96 / kMfma + 1;   // vector instructions between two of them
+    if constexpr (!LAST) tmax_n = row_max(sc[1 - PAR]);
+    constexpr int kMfma = DB * 4 + (LAST ? 0 : 2 * NQ);  // matrix instructions in the block
+    // Vector instructions between two of them: about 96 per full block. The last block
+    // keeps the same spacing (a denser one raised the register pressure past the budget).
+    constexpr int kValu = 96 / (DB * 4 + 2 * NQ) + 1;
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
 #pragma unroll
     for (int i = 0; i < kMfma / 2; ++i) {
@@ -456,17 +470,32 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
   };
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
+  using Inner = std::integral_constant<bool, false>;
+  using Last = std::integral_constant<bool, true>;
   int j = lo;
-  if (j & 1) iter(std::integral_constant<int, 1>{}, j++);
-  for (; j <= hi; j += 2) {
-    iter(std::integral_constant<int, 0>{}, j);
-    if (j + 1 <= hi) iter(std::integral_constant<int, 1>{}, j + 1);
+  if ((j & 1) && j < hi) iter(Odd{}, Inner{}, j++);
+  for (; j + 1 < hi; j += 2) {  // j even
+    iter(Even{}, Inner{}, j);
+    iter(Odd{}, Inner{}, j + 1);
   }
-  if (moved_p) scale_o(alpha_p);
+  if (j < hi) iter(Even{}, Inner{}, j++);  // j was hi - 1, even
   if (hi & 1)
-    pv(std::integral_constant<int, 3 * TILEB>{}, pr[1]);
+    iter(Odd{}, Last{}, hi);
   else
-    pv(std::integral_constant<int, 2 * TILEB>{}, pr[0]);
+    iter(Even{}, Last{}, hi);
+  if (moved_p) scale_o(alpha_p);
+  // The last value product, unless no row of this wave sees a key of tile hi (the first
+  // rows of a workgroup whose last tile lies past them): its probabilities are all zero.
+  // (Full only: with the window's extra live values this branch pushed the sliding kernel
+  // past its register budget.)
+  if (kSlide || hi * BN <= q0 + wave_s * 32 + 31) {  // the wave's first row, as a scalar
+    if (hi & 1)
+      pv(std::integral_constant<int, 3 * TILEB>{}, pr[1]);
+    else
+      pv(std::integral_constant<int, 2 * TILEB>{}, pr[0]);
+  }
 
   // ---- epilogue: out = O / l. Element (db, r) of a lane is channel
   // db*32 + 8*(r/4) + 4*lg + r%4 of query qi.
