@@ -60,12 +60,17 @@ namespace dma {
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-// Launch shape of the full and sliding kernel: 4 waves of 32 query rows per workgroup.
-// Register budget: two waves per SIMD, i.e. two independent workgroups per CU.
+// Launch shape of the full and sliding kernel: 4 row blocks of 32 query rows per workgroup,
+// each served by SPL waves. SPL = 1: 4 waves, two workgroups per CU (two waves per SIMD).
+// SPL = 2 (key split, for grids of at most one workgroup per CU): 8 waves, the two waves of
+// a row block take alternate key tiles and merge their softmax states at the end; one
+// workgroup per CU, two waves per SIMD. The register budget is two waves per SIMD either way.
+template <int SPL>
 struct DShape {
-  static constexpr int waves = 4;
+  static constexpr int rows = 4;  // 32-row blocks
+  static constexpr int waves = rows * SPL;
   static constexpr int threads = waves * kWave;
-  static constexpr int bm = 32 * waves;
+  static constexpr int bm = 32 * rows;
 };
 
 // Chunk swizzle of a tile row: the 16-byte chunk c of row r is stored at chunk c ^ swz(r).
@@ -138,16 +143,19 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-template <int D, int VAR>
-__global__ void __attribute__((amdgpu_flat_work_group_size(DShape::threads, DShape::threads),
+template <int D, int VAR, int SPL>
+__global__ void __attribute__((amdgpu_flat_work_group_size(DShape<SPL>::threads,
+                                                           DShape<SPL>::threads),
                                amdgpu_waves_per_eu(2, 2)))
 prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
                    const __bf16* __restrict__ vg, __bf16* __restrict__ og, int L, int BH,
                    int G, int nq, int window) {
   static_assert(VAR == kFull || VAR == kSliding, "the differential has its own kernel");
+  static_assert(SPL == 1 || SPL == 2, "one or two waves per row block");
   constexpr bool kSlide = (VAR == kSliding);
-  constexpr int kWaves = DShape::waves;
-  constexpr int BM = DShape::bm;
+  constexpr int kWaves = DShape<SPL>::waves;
+  constexpr int kRows = DShape<SPL>::rows;
+  constexpr int BM = DShape<SPL>::bm;
   constexpr int NQ = D / 16;                      // MFMA steps over the head dim
   constexpr int DB = D / 32;                      // 32-channel blocks of O^T
   constexpr int ROWB = D * 2;                     // bytes per K/V row
@@ -157,16 +165,24 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   constexpr int CPR = D / 8;                      // 16-byte chunks per row
   static_assert(NI % kWaves == 0, "tile loads must split evenly over the waves");
 
-  // LDS: K buffers 0, 1 then V buffers 0, 1.
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];
+  // LDS: K buffers 0, 1 then V buffers 0, 1; buffer b of a kind holds the SPL tiles of
+  // iterations of parity b (tile s of the iteration at s * TILEB). With SPL = 2 the same
+  // memory passes the second wave's softmax state to the first at the end.
+  __shared__ __attribute__((aligned(1024))) char smem[4 * SPL * TILEB];
   lds_char* const lds = (lds_char*)(smem);
   const unsigned lds_addr = (unsigned)(uintptr_t)lds;  // LDS byte address of smem
+  // Byte offset of the K (V) buffer of parity b within smem.
+  constexpr int kKBuf[2] = {0, SPL * TILEB};
+  constexpr int kVBuf[2] = {2 * SPL * TILEB, 3 * SPL * TILEB};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // the same value, in an SGPR
-  const int rb = wave;  // row block of this wave
+  const int rb = SPL == 1 ? wave : wave % kRows;       // row block of this wave
+  const int half = SPL == 1 ? 0 : wave / kRows;        // its tile of each iteration
+  const int rb_s = SPL == 1 ? wave_s : wave_s % kRows;  // the same two, in SGPRs
+  const int half_s = SPL == 1 ? 0 : wave_s / kRows;
   const int lr = lane & 31;
   const int lg = lane >> 5;
 
@@ -205,12 +221,19 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   // K operand reads: row kb*32 + lr (the swizzle depends on the row mod 16 only), chunk
   // 2*kk + lg.
   const int k_sw = swz<D>(lr);
+  // The wave's tile within its iteration's buffer is folded into the per-lane offsets.
   int k_off[NQ];
 #pragma unroll
-  for (int kk = 0; kk < NQ; ++kk) k_off[kk] = lr * ROWB + (((2 * kk + lg) ^ k_sw) << 4);
+  for (int kk = 0; kk < NQ; ++kk)
+    k_off[kk] = half * TILEB + lr * ROWB + (((2 * kk + lg) ^ k_sw) << 4);
   // V^T operand reads (transposed, 8 bytes per lane): for the 16-key half h of key block kb
   // and read rr, lane (group g = lane/16, s = lane%16) reads key row
   // kb*32 + 16h + 8rr + 4*lg + s/4, channels db*32 + 16*(g%2) + 4*(s%4) + [0, 4).
+  // With SPL = 2 the V region starts at 64 KiB (d = 128), past what a DS instruction's
+  // offset field holds: its base goes into the per-lane offsets, so that every immediate
+  // stays below 64 KiB. With SPL = 1 the whole V buffer offset is an immediate.
+  constexpr int kVOffBase = SPL == 1 ? 0 : kVBuf[0];
+  constexpr int kVImm[2] = {kVBuf[0] - kVOffBase, kVBuf[1] - kVOffBase};
   const int vs = lane & 15, vdh = (lane >> 4) & 1;
   int v_off[DB][2];
 #pragma unroll
@@ -219,13 +242,17 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
     for (int rr = 0; rr < 2; ++rr) {
       const int r = 8 * rr + 4 * lg + (vs >> 2);
       const int chunk = 4 * db + 2 * vdh + ((vs & 3) >> 1);
-      v_off[db][rr] = r * ROWB + ((chunk ^ swz<D>(r)) << 4) + (vs & 1) * 8;
+      v_off[db][rr] = kVOffBase + half * TILEB + r * ROWB + ((chunk ^ swz<D>(r)) << 4) +
+                      (vs & 1) * 8;
     }
 
-  // ---- key tiles the workgroup can see: [lo, hi]
+  // ---- key tiles the workgroup can see: [lo, hi]. Iteration it takes tiles
+  // lo + SPL*it + s (s < SPL), the one at s = half for this wave; with SPL = 2 the second
+  // wave's tile of the last iteration may be hi + 1, which no row sees (it is masked).
   const int q_last = min(q0 + BM, L) - 1;
   const int lo = kSlide ? max(0, q0 - window + 1) / BN : 0;
   const int hi = q_last / BN;
+  const int n_it = (hi - lo) / SPL + 1;
 
   // LDS byte offsets of the K and V buffers holding tile j.
   // Tile j of K (v = false) or V (v = true) into the LDS buffer at byte offset `dst`.
@@ -237,6 +264,11 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
 #pragma unroll
     for (int t = 0; t < NIW; ++t)
       lds_load16(r, (unsigned)(lds_addr + dst + (wave_s + t * kWaves) * 1024), ld_off[t]);
+  };
+  // The SPL tiles of iteration it into the buffer at byte offset `dst`.
+  auto load_it = [&](bool v, int dst, int it) {
+#pragma unroll
+    for (int s = 0; s < SPL; ++s) load_tile(v, dst + s * TILEB, lo + SPL * it + s);
   };
   // Does every row of the wave see every key of tile j?
   auto full_tile = [&](int j) {
@@ -356,14 +388,14 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
       for (int r = 0; r < 16; ++r) o[db][r] *= f;
   };
 
-  // ---- prologue: zero both V buffers (the first iteration multiplies P = 0 by the buffer
-  // of tile lo-1, which must hold finite values); K[lo], K[lo+1] into LDS; S = K[lo] Q^T
-  // and its row max.
+  // ---- prologue: zero the V buffer of parity 1 (iteration 0 multiplies P = 0 by it, which
+  // must hold finite values); the K tiles of iterations 0 and 1 into LDS; S = K Q^T of the
+  // wave's tile of iteration 0 and its row max.
   {
     const floatx4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-    floatx4* const vz = reinterpret_cast<floatx4*>(smem + 2 * TILEB);
+    floatx4* const vz = reinterpret_cast<floatx4*>(smem + kVBuf[1]);
 #pragma unroll
-    for (int i = tid; i < 2 * TILEB / 16; i += kWaves * kWave) vz[i] = z;
+    for (int i = tid; i < SPL * TILEB / 16; i += kWaves * kWave) vz[i] = z;
   }
 #pragma unroll
   for (int t = 0; t < 2; ++t)
@@ -373,50 +405,52 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) pr[t][kb][h][e] = (__bf16)0.0f;
-  load_tile(false, (lo & 1) * TILEB, lo);
-  if (lo + 1 <= hi) load_tile(false, ((lo + 1) & 1) * TILEB, lo + 1);
+  load_it(false, kKBuf[0], 0);
+  if (n_it > 1) load_it(false, kKBuf[1], 1);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
   // The first tile's scores, unless no row of this wave sees any of its keys (a wave below
-  // the window of the workgroup's first rows): then zeros stand in, and the mask of the
-  // first iteration turns every one of them into -inf.
-  const bool see_lo = kSlide ? (lo * BN + BN - 1 >= q0 + wave_s * 32 - window + 1) : true;
+  // the window of the workgroup's first rows, or a second wave's tile past its rows): then
+  // zeros stand in, and the mask of the first iteration turns every one of them into -inf.
+  const int j0_s = lo + half_s;
+  const int qw_s = q0 + rb_s * 32;  // the wave's first row, as a scalar
+  // (Not for sliding with SPL = 1, where the branch pushed the kernel past its register
+  // budget.)
+  const bool see_first = (kSlide && SPL == 1) ||
+                         ((half_s == 0 || j0_s * BN <= qw_s + 31) &&
+                          (!kSlide || j0_s * BN + BN - 1 >= qw_s - window + 1));
   float tmax_n;  // row max of the scores of the next tile (unmasked)
-  auto first_scores = [&](auto koff_c, floatx16(&d)[2]) {
-    if (see_lo) {
-      qk_into(koff_c, d);
-    } else {
+  if (see_first) {
+    qk_into(std::integral_constant<int, kKBuf[0]>{}, sc[0]);
+  } else {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) d[kb][r] = 0.0f;
-    }
-    tmax_n = row_max(d);
-  };
-  if (lo & 1)
-    first_scores(std::integral_constant<int, TILEB>{}, sc[1]);
-  else
-    first_scores(std::integral_constant<int, 0>{}, sc[0]);
+      for (int r = 0; r < 16; ++r) sc[0][kb][r] = 0.0f;
+  }
+  tmax_n = row_max(sc[0]);
   __syncthreads();
 
-  // ---- key loop. Every wave runs the same sequence on every tile of the workgroup's
+  // ---- key loop. Every wave runs the same sequence on every iteration of the workgroup's
   // range: keys a wave cannot see are masked (probability 0, softmax state unchanged), so
   // the loop body is one straight path and the register allocation stays within two waves
   // per SIMD.
   float alpha_p = 1.0f;  // pending rescale of O, decided on the previous tile
   bool moved_p = false;
-  // One iteration on tile j, with PAR = j & 1; LAST marks tile hi, whose iteration has no
-  // next tile to score.
-  auto iter = [&](auto par_c, auto last_c, int j) {
+  // Iteration it, with PAR = it & 1, on this wave's tile j = lo + SPL*it + half; LAST marks
+  // the last iteration, which has no next tile to score.
+  auto iter = [&](auto par_c, auto last_c, int it) {
     constexpr int PAR = decltype(par_c)::value;
     constexpr bool LAST = decltype(last_c)::value;
-    // Loads for the next iteration, issued first: K[j+2] into K's buffer PAR (K[j] was read
-    // during iteration j-1), while tile j+2 is in the workgroup's range, and V[j] into V's
-    // buffer PAR (V[j-2] was read during j-1).
-    if (!LAST && j + 2 <= hi) load_tile(false, PAR * TILEB, j + 2);
-    load_tile(true, (2 + PAR) * TILEB, j);
-    // Rescale decided on tile j-1: O holds tiles up to j-2 here, and the value product of
-    // tile j-1 below is already on tile j-1's reference.
+    const int j = lo + SPL * it + half;
+    // Loads for the next iteration, issued first: the K tiles of iteration it+2 into K's
+    // buffer PAR (those of iteration it were read during it-1), while it+2 is in the range,
+    // and the V tiles of iteration it into V's buffer PAR (those of it-2 were read during
+    // it-1).
+    if (!LAST && it + 2 < n_it) load_it(false, kKBuf[PAR], it + 2);
+    load_it(true, kVBuf[PAR], it);
+    // Rescale decided on the previous tile: O holds the tiles before that one here, and the
+    // value product of the previous tile below is already on its reference.
     if (moved_p) scale_o(alpha_p);
     // Row max of tile j: taken during the previous iteration, again here after the mask
     // on tiles that cross the diagonal or the window edge.
@@ -434,20 +468,22 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
       l *= alpha;
       m = m_new;
     }
-    // One straight block: S[j+1] = K[j+1] Q^T first (not on the last tile), then
-    // O += V[j-1] P[j-1]; beside them the exponentials of tile j and, once S[j+1] is in,
-    // its row max. The group barriers fix the issue order so that vector work sits between
-    // the matrix instructions: a wave issues in order, and an MFMA waiting for the busy
-    // matrix pipe holds up everything behind it.
-    if constexpr (!LAST) qk_into(std::integral_constant<int, (1 - PAR) * TILEB>{}, sc[1 - PAR]);
-    pv(std::integral_constant<int, (3 - PAR) * TILEB>{}, pr[1 - PAR]);
+    // One straight block: the next tile's S = K Q^T first (not in the last iteration), then
+    // O += V P of the previous tile; beside them the exponentials of tile j and, once the
+    // next S is in, its row max. The group barriers fix the issue order so that vector work
+    // sits between the matrix instructions: a wave issues in order, and an MFMA waiting for
+    // the busy matrix pipe holds up everything behind it.
+    if constexpr (!LAST)
+      qk_into(std::integral_constant<int, kKBuf[1 - PAR]>{}, sc[1 - PAR]);
+    pv(std::integral_constant<int, kVImm[1 - PAR]>{}, pr[1 - PAR]);
     exps(sc[PAR], pr[PAR]);
     if constexpr (!LAST) tmax_n = row_max(sc[1 - PAR]);
-    constexpr int kMfma = DB * 4 + (LAST ? 0 : 2 * NQ);  // matrix instructions in the block
-    // Vector instructions between two of them: about 96 per full block. The last block
-    // keeps the same spacing (a denser one raised the register pressure past the budget).
-    constexpr int kValu = 96 / (DB * 4 + 2 * NQ) + 1;
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+    // Matrix instructions in the block, and vector instructions between two of them (about
+    // 110 per block). The last block is left to the compiler's own order: every fixed
+    // spacing tried there pushed the register pressure past the budget.
+    constexpr int kMfma = LAST ? 0 : DB * 4 + 2 * NQ;
+    constexpr int kValu = 110 / (DB * 4 + 2 * NQ) + 1;
+    if constexpr (!LAST) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
 #pragma unroll
     for (int i = 0; i < kMfma / 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
@@ -474,41 +510,75 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   using Odd = std::integral_constant<int, 1>;
   using Inner = std::integral_constant<bool, false>;
   using Last = std::integral_constant<bool, true>;
-  int j = lo;
-  if ((j & 1) && j < hi) iter(Odd{}, Inner{}, j++);
-  for (; j + 1 < hi; j += 2) {  // j even
-    iter(Even{}, Inner{}, j);
-    iter(Odd{}, Inner{}, j + 1);
+  int it = 0;
+  for (; it + 2 < n_it; it += 2) {  // it even; it and it + 1 both before the last
+    iter(Even{}, Inner{}, it);
+    iter(Odd{}, Inner{}, it + 1);
   }
-  if (j < hi) iter(Even{}, Inner{}, j++);  // j was hi - 1, even
-  if (hi & 1)
-    iter(Odd{}, Last{}, hi);
+  if (it + 1 < n_it) iter(Even{}, Inner{}, it++);  // it was n_it - 2
+  if (it & 1)
+    iter(Odd{}, Last{}, it);
   else
-    iter(Even{}, Last{}, hi);
+    iter(Even{}, Last{}, it);
   if (moved_p) scale_o(alpha_p);
-  // The last value product, unless no row of this wave sees a key of tile hi (the first
-  // rows of a workgroup whose last tile lies past them): its probabilities are all zero.
-  // (Full only: with the window's extra live values this branch pushed the sliding kernel
-  // past its register budget.)
-  if (kSlide || hi * BN <= q0 + wave_s * 32 + 31) {  // the wave's first row, as a scalar
-    if (hi & 1)
-      pv(std::integral_constant<int, 3 * TILEB>{}, pr[1]);
+  // The last value product, unless no row of this wave sees a key of its last tile (the
+  // first rows of a workgroup whose last tile lies past them): its probabilities are all
+  // zero. (Not for sliding with SPL = 1: with the window's extra live values this branch
+  // pushed that kernel past its register budget.)
+  const int jl_s = lo + SPL * it + half_s;
+  if ((kSlide && SPL == 1) || jl_s * BN <= qw_s + 31) {
+    if (it & 1)
+      pv(std::integral_constant<int, kVImm[1]>{}, pr[1]);
     else
-      pv(std::integral_constant<int, 2 * TILEB>{}, pr[0]);
+      pv(std::integral_constant<int, kVImm[0]>{}, pr[0]);
   }
 
   // ---- epilogue: out = O / l. Element (db, r) of a lane is channel
-  // db*32 + 8*(r/4) + 4*lg + r%4 of query qi.
-  const float lsum = xhalf_sum(l);
-  if (qi < L) {
+  // db*32 + 8*(r/4) + 4*lg + r%4 of query qi. The lane's indices are taken afresh here (the
+  // lane number from mbcnt, the rest from scalars), so nothing but O, l and m has to stay
+  // live through the key loop for it.
+  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int lg_e = lane_e >> 5;
+  const int qi_e = q0 + rb_s * 32 + (lane_e & 31);
+  float lsum = xhalf_sum(l);
+  if constexpr (SPL == 2) {
+    // The second wave of each row block hands its state (reference m, row sum, O) to the
+    // first through LDS; the first rescales both to the larger reference and adds them.
+    constexpr int kXch = 64 * (DB * 16 + 2);  // floats per row block
+    static_assert(kRows * kXch * 4 <= 4 * SPL * TILEB, "exchange fits the tile buffers");
+    __syncthreads();  // every wave is done reading the tiles
+    float* const xch = reinterpret_cast<float*>(smem) + rb_s * kXch;
+    if (half_s == 1) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xch[(db * 16 + r) * 64 + lane_e] = o[db][r];
+      xch[DB * 16 * 64 + lane_e] = m;
+      xch[(DB * 16 + 1) * 64 + lane_e] = lsum;
+    }
+    __syncthreads();
+    if (half_s == 1) return;
+    const float m1 = xch[DB * 16 * 64 + lane_e];
+    const float l1 = xch[(DB * 16 + 1) * 64 + lane_e];
+    const float mm = __builtin_fmaxf(m, m1);  // finite: every row sees its own key
+    const float a0 = (m == -INFINITY) ? 0.0f : fast_exp2((m - mm) * c);
+    const float a1 = (m1 == -INFINITY) ? 0.0f : fast_exp2((m1 - mm) * c);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        o[db][r] = o[db][r] * a0 + xch[(db * 16 + r) * 64 + lane_e] * a1;
+    lsum = lsum * a0 + l1 * a1;
+  }
+  if (qi_e < L) {
     const float inv = 1.0f / lsum;
-    __bf16* orow = og + head + (size_t)qi * D;
+    __bf16* orow = og + head + (size_t)qi_e * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
-        store4(orow + db * 32 + 8 * r4 + 4 * lg, o[db][r4 * 4] * inv, o[db][r4 * 4 + 1] * inv,
-               o[db][r4 * 4 + 2] * inv, o[db][r4 * 4 + 3] * inv);
+        store4(orow + db * 32 + 8 * r4 + 4 * lg_e, o[db][r4 * 4] * inv,
+               o[db][r4 * 4 + 1] * inv, o[db][r4 * 4 + 2] * inv, o[db][r4 * 4 + 3] * inv);
   }
 }
 
@@ -840,16 +910,31 @@ prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg
 
 
 
-template <int D, int VAR>
-hipError_t launch_dma_t(const PrefillLaunch& a, hipStream_t stream) {
-  constexpr int BM = DShape::bm;
-  const int nq = (a.L + BM - 1) / BM;
+template <int D, int VAR, int SPL>
+hipError_t launch_dma_s(const PrefillLaunch& a, int nq, hipStream_t stream) {
   const int BH = a.B * a.H;
-  hipLaunchKernelGGL((prefill_dma_kernel<D, VAR>), dim3((unsigned)(BH * nq)),
-                     dim3(DShape::threads), 0, stream, static_cast<const __bf16*>(a.q),
+  hipLaunchKernelGGL((prefill_dma_kernel<D, VAR, SPL>), dim3((unsigned)(BH * nq)),
+                     dim3(DShape<SPL>::threads), 0, stream, static_cast<const __bf16*>(a.q),
                      static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
                      static_cast<__bf16*>(a.out), a.L, BH, a.H / a.Hkv, nq, a.window);
   return hipGetLastError();
+}
+
+// Full and sliding: the key split (SPL = 2) when the grid holds at most one workgroup per
+// CU, where the 4-wave workgroups would leave one wave per SIMD and the longest query tile
+// alone would set the time; otherwise two 4-wave workgroups per CU.
+template <int D, int VAR>
+hipError_t launch_dma_t(const PrefillLaunch& a, hipStream_t stream) {
+  constexpr int BM = DShape<1>::bm;
+  static_assert(DShape<2>::bm == BM, "both shapes tile the rows alike");
+  const int nq = (a.L + BM - 1) / BM;
+  const long long wgs = (long long)a.B * a.H * nq;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  return wgs <= cus ? launch_dma_s<D, VAR, 2>(a, nq, stream)
+                    : launch_dma_s<D, VAR, 1>(a, nq, stream);
 }
 
 template <int D>
