@@ -14,8 +14,15 @@ Reported (one JSON line):
                   query-key pair, summed over the nine layers, / step time);
   per_variant     per-layer kernel time and useful TFLOP/s of each variant at L=8K, from HIP
                   events recorded between the launches inside the timed steps, and the
-                  fraction of the dense bf16 MFMA peak;
-  roofline        the same for the kernel that takes most of the step time;
+                  fraction of the dense bf16 MFMA peak; the executed rate counts the matrix
+                  instructions of the kernel's own tile schedule (masked keys of whole tiles,
+                  the differential's second value product); the matrix-pipe busy share and
+                  effective clock come from the committed SQ counter summary while it matches
+                  the kernel source;
+  roofline        the same for the kernel that takes most of the step time, with its HBM
+                  traffic and matrix-pipe busy share from the committed counter summaries;
+  sweep           the other lengths of Table 3 (sec. 4.2): full at L=2K and 32K, the
+                  differential at 32K (on by default; --no-sweep skips it);
   memory          peak device memory of one isolated layer at L = 2K, 8K, 32K: q, k, v and
                   out, and the drop in free device memory across the launches (0: the
                   library allocates nothing);
@@ -26,14 +33,15 @@ Reported (one JSON line):
                   (each variant's share is in per_variant);
   gqa             one layer per variant at the model's grouped-head shape (16 heads over
                   4 KV heads, Table 2), timed with HIP events;
-  cpu_baseline    the fp64 oracle on the same nine layers, every row (host cores).
+  cpu_baseline    the fp64 oracle on the same nine layers, every row (host cores, with
+                  the thread count it used and the CPU model).
 
 Timing starts at the working clock: the GPU lowers its clock while the host draws the
 inputs, so 0.3 s of untimed stack steps (--settle) run before the W warm-up steps, and the
 timed region is exactly the K steps after those.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle SECONDS]
-       [--no-cpu-baseline] [--no-gqa] [--no-extras] [--copy-calibration] [--sweep]
+       [--no-cpu-baseline] [--no-gqa] [--no-extras] [--copy-calibration] [--no-sweep]
 """
 from __future__ import annotations
 
@@ -54,6 +62,10 @@ PEAK_BF16_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
 VARIANT_NAMES = ("full", "sliding", "differential")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+SQ_FILE = os.path.join(ROOT, "profiles", "sq_busy.txt")
+# MI355X: 8 XCDs of 32 CUs, 4 SIMDs per CU.
+N_XCD, N_CU, N_SIMD = 8, 256, 1024
+MFMA_FLOPS = 32 * 32 * 16 * 2  # one v_mfma_f32_32x32x16_bf16
 # Sources of the bf16 kernel the bench times (a traffic summary is valid only for them).
 KERNEL_SOURCES = [os.path.join(ROOT, "heterogeneous_attention_mixer_amd", "csrc", f)
                   for f in ("attn_prefill_dma.hip", "device_common.h", "kernels.h")]
@@ -78,10 +90,52 @@ def useful_flops(variant: str, B: int, H: int, L: int, d: int, window: int) -> i
     return 4 * d * B * H * visible_pairs(variant, L, window)
 
 
-def executed_per_useful(variant: str) -> float:
-    """Flops the single-pass kernel executes per useful flop: the differential runs two value
-    products (one per map), 6*d per pair instead of 4*d."""
-    return 1.5 if variant == "differential" else 1.0
+def executed_mfmas(variant: str, B: int, H: int, L: int, d: int, window: int,
+                   n_cu: int = N_CU) -> int:
+    """Matrix instructions (v_mfma_f32_32x32x16_bf16) one launch of the bf16 kernel issues,
+    counted from the same tile schedule the kernels follow: whole 64-key tiles, 32 query rows
+    per wave, masked keys computed like visible ones.
+
+    Full and sliding (128 query rows per workgroup, 4 row blocks): per wave, the scores of
+    its first tile in the prologue, then per iteration the next tile's scores and the
+    previous tile's value product (the first iteration's value product multiplies zero
+    probabilities), the last iteration only the value product, and the value product of the
+    last tile after the loop. With at most one workgroup per CU the key split runs (two
+    waves per row block, alternate tiles); otherwise one wave per row block. A wave skips
+    the first scores of a tile no row of it sees and the last value product of a tile past
+    its rows, where the kernel does (see the kernel's prologue and tail).
+    Differential (8 waves: 4 row blocks x 2 maps): per wave hi + 2 matrix phases of the
+    half-width scores and the full-width value product each."""
+    bm, bn = 128, 64
+    nq = (L + bm - 1) // bm
+    qk = 2 * (d // 16)          # one tile's scores: 2 key blocks x d/16 steps
+    pv = 2 * 2 * (d // 32)      # one tile's value product: 4 key groups x d/32 channel blocks
+    slide = variant == "sliding"
+    total = 0
+    if variant == "differential":
+        qk_half = 2 * (d // 32)
+        for qt in range(nq):
+            hi = (min(qt * bm + bm, L) - 1) // bn
+            total += 8 * (hi + 2) * (qk_half + pv)
+        return B * H * total
+    spl = 2 if B * H * nq <= n_cu else 1
+    for qt in range(nq):
+        q0 = qt * bm
+        hi = (min(q0 + bm, L) - 1) // bn
+        lo = max(0, q0 - window + 1) // bn if slide else 0
+        n_it = (hi - lo) // spl + 1
+        for rb in range(4):
+            qw = q0 + 32 * rb
+            for half in range(spl):
+                j0 = lo + half
+                see_first = (slide and spl == 1) or (
+                    (half == 0 or j0 * bn <= qw + 31) and
+                    (not slide or j0 * bn + bn - 1 >= qw - window + 1))
+                jl = lo + spl * (n_it - 1) + half
+                tail = (slide and spl == 1) or jl * bn <= qw + 31
+                total += (qk if see_first else 0) + (n_it - 1) * (qk + pv) + pv + \
+                    (pv if tail else 0)
+    return B * H * total
 
 
 def _code_only(text: str) -> str:
@@ -117,6 +171,97 @@ def read_traffic(variant: str):
         return None
     key = f"{variant}_hbm_bytes_per_launch"
     return float(kv[key]) if key in kv else None
+
+
+def _read_kv(path):
+    kv = {}
+    if not os.path.exists(path):
+        return kv
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    return kv
+
+
+def read_sq(variant: str):
+    """Matrix-pipe busy fraction and MFMA count per launch of ``variant`` from the committed
+    SQ counter summary, or None when there is none or the kernel source changed since the
+    counters were taken."""
+    kv = _read_kv(SQ_FILE)
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return {"mfma_busy": float(kv[f"{variant}_mfma_busy"]),
+                "sq_insts_mfma": int(float(kv[f"{variant}_sq_insts_mfma"])),
+                "effective_clock_ghz": float(kv[f"{variant}_effective_clock_ghz"])}
+    except KeyError:
+        return None
+
+
+def write_sq(csv_path: str, command: str) -> str:
+    """Turn one rocprofv3 --pmc run (SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA, GRBM_GUI_ACTIVE,
+    with --kernel-trace) over the bench's stack into SQ_FILE, keyed to the kernel source
+    hash: per d=128 bf16 variant the matrix pipe's busy share of the dispatch's cycles
+    (busy cycles per SIMD over GUI-active cycles per XCD), the MFMA count per launch, and the
+    effective clock (GUI-active cycles per XCD over the dispatch's duration)."""
+    import csv
+    vals = {}
+    dur = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            key = next((v for v, (_, tag) in KERNELS.items() if tag in name), None)
+            if key is None:
+                continue
+            did = r.get("Dispatch_Id", "")
+            vals.setdefault(key, {}).setdefault(r["Counter_Name"], {})[did] = float(
+                r["Counter_Value"])
+            if "End_Timestamp" in r and "Start_Timestamp" in r:
+                dur.setdefault(key, {})[did] = (int(r["End_Timestamp"]) -
+                                                int(r["Start_Timestamp"]))
+    lines = ["# Matrix-pipe busy share, MFMA count and effective clock per launch of the d=128",
+             "# bf16 kernel of each variant at B=1 H=16 L=8192 (Latin stack workload), from one",
+             "# rocprofv3 --pmc run with --kernel-trace, averaged over the stack's launches.",
+             "# mfma_busy = (SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs) / (GRBM_GUI_ACTIVE / 8 XCDs);",
+             "# effective_clock_ghz = (GRBM_GUI_ACTIVE / 8) / dispatch duration.",
+             f"# command: {command}",
+             f"kernel_source_sha256_16 = {kernel_source_hash()}"]
+    for v in VARIANT_NAMES:
+        c = vals.get(v, {})
+        need = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE")
+        if not all(n in c for n in need):
+            continue
+        ids = sorted(set.intersection(*(set(c[n]) for n in need)))
+        busy = [c["SQ_VALU_MFMA_BUSY_CYCLES"][i] / N_SIMD / (c["GRBM_GUI_ACTIVE"][i] / N_XCD)
+                for i in ids]
+        insts = [c["SQ_INSTS_MFMA"][i] for i in ids]
+        clk = [c["GRBM_GUI_ACTIVE"][i] / N_XCD / dur[v][i]
+               for i in ids if dur.get(v, {}).get(i)]
+        lines.append(f"{v}_mfma_busy = {sum(busy) / len(busy):.4f}")
+        lines.append(f"{v}_sq_insts_mfma = {sum(insts) / len(insts):.0f}")
+        if clk:
+            lines.append(f"{v}_effective_clock_ghz = {sum(clk) / len(clk):.4f}")
+        lines.append(f"{v}_dispatches = {len(ids)}")
+    os.makedirs(os.path.dirname(SQ_FILE), exist_ok=True)
+    with open(SQ_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return SQ_FILE
+
+
+def cpu_model() -> str:
+    """The host CPU's model name as the kernel reports it (Linux), or the platform string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
 
 
 COPY_BYTES = 256 * 1024 * 1024  # the --copy-calibration copy: reads and writes this much
@@ -197,6 +342,8 @@ def cpu_baseline(host_layers, sched, cfg, rows_per_head: int):
         "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.max_threads(),
+        "cpu_model": cpu_model(),
+        "host_logical_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": (f"{what} of all {len(host_layers)} layers of one step of the stack "
                    f"(full, sliding W={cfg['window']}, differential lambda={cfg['lam']}), "
@@ -224,18 +371,27 @@ def main(argv=None) -> int:
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the memory and placement-arm sections (profiling runs, as "
                          "for --no-gqa)")
-    ap.add_argument("--sweep", action="store_true",
-                    help="also time full at L=2K/32K and differential at L=32K")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the other lengths of Table 3 (full at L=2K/32K, differential at "
+                         "L=32K), which run by default; for profiling runs")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="host only: write the HBM traffic summary from two rocprofv3 "
                          "counter files and exit")
     ap.add_argument("--traffic-command", default="",
-                    help="with --write-traffic: the profiling command, recorded in the file")
+                    help="with --write-traffic or --write-sq: the profiling command, recorded "
+                         "in the file")
+    ap.add_argument("--write-sq", metavar="COUNTER_CSV",
+                    help="host only: write the matrix-pipe busy summary from one rocprofv3 "
+                         "counter file (SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA, "
+                         "GRBM_GUI_ACTIVE, with --kernel-trace) and exit")
     args = ap.parse_args(argv)
 
     if args.write_traffic:
         print(write_traffic(args.write_traffic[0], args.write_traffic[1],
                             args.traffic_command))
+        return 0
+    if args.write_sq:
+        print(write_sq(args.write_sq, args.traffic_command))
         return 0
 
     if args.gpus != 1:
@@ -343,6 +499,7 @@ def main(argv=None) -> int:
             continue
         ms = sum(ts) / len(ts)
         fl = useful_flops(name, B, H, L, d, W)
+        ex = executed_mfmas(name, B, H, L, d, W) * MFMA_FLOPS
         srt = sorted(ts)
         per_variant[name] = {
             "ms_per_launch": round(ms, 5),
@@ -350,10 +507,15 @@ def main(argv=None) -> int:
             "ms_min": round(srt[0], 5),
             "launches": len(ts),
             "useful_tflops": round(fl / (ms * 1e-3) / 1e12, 2),
-            "executed_tflops": round(fl * executed_per_useful(name) / (ms * 1e-3) / 1e12, 2),
+            "executed_tflops": round(ex / (ms * 1e-3) / 1e12, 2),
+            "executed_per_useful": round(ex / fl, 4),
             "frac_of_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "useful_gflop_per_launch": round(fl / 1e9, 3),
         }
+        sq = read_sq(name)
+        if sq:
+            per_variant[name]["mfma_busy"] = sq["mfma_busy"]
+            per_variant[name]["effective_clock_ghz"] = sq["effective_clock_ghz"]
     dominant = max(per_variant, key=lambda n: per_variant[n]["ms_per_launch"]
                    * per_variant[n]["launches"])
     dom = per_variant[dominant]
@@ -366,6 +528,7 @@ def main(argv=None) -> int:
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
         "traffic": read_traffic(dominant),
+        "mfma_busy": (read_sq(dominant) or {}).get("mfma_busy"),
     }
 
     # Peak device memory of one isolated layer (Table 3's memory column): the high-water mark
@@ -493,7 +656,7 @@ def main(argv=None) -> int:
     del gqa_inputs
 
     sweep = None
-    if args.sweep:
+    if not args.no_sweep:
         sweep = {}
         for name, variant, Ls in (("full", "full", (2048, 32768)),
                                   ("differential", "differential", (32768,))):
@@ -514,9 +677,11 @@ def main(argv=None) -> int:
                 torch.cuda.synchronize()
                 ms = e0.elapsed_time(e1) / reps
                 fl = useful_flops(variant, B, H, Lx, d, 0)
+                ex = executed_mfmas(variant, B, H, Lx, d, 0) * MFMA_FLOPS
                 sweep[f"{name}_L{Lx}"] = {
                     "ms_per_launch": round(ms, 5),
                     "useful_tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                    "executed_per_useful": round(ex / fl, 4),
                     "frac_of_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                                4)}
                 del t, o

@@ -17,8 +17,11 @@
  *     hipStream_t passed as void*, NULL = the legacy default stream) and return. Launch
  *     errors come back as MIXER_EHIP; a fault during execution surfaces at the caller's next
  *     synchronisation. Calls on different streams may run from different threads.
- *   - Validation is host-only and happens before any HIP call: a call that returns an error
- *     code has not touched the device.
+ *   - Validation is host-only and happens before any HIP call: a call that returns
+ *     MIXER_EINVAL, MIXER_EUNSUPPORTED or MIXER_ENOTLATIN has not touched the device.
+ *     MIXER_EHIP means the runtime refused a launch or an event record; the single-layer
+ *     calls have then enqueued nothing, the multi-layer runners may have enqueued the layers
+ *     before the failing one (see mixer_layers_prefill).
  *   - Scores are scaled by 1/sqrt(d) (full, sliding) or 1/sqrt(d/2) (differential); there
  *     is no scale argument.
  *   - Arithmetic: bf16 operands on the matrix cores with fp32 accumulation; softmax in fp32;
@@ -135,7 +138,8 @@ int mixer_latin_check(int N, const int *sched);
  * layer_events    NULL, or a host array of N*N + 1 hipEvent_t (passed as void*): event 0
  *                 is recorded before layer 0 and event l + 1 after layer l.
  * Every layer's arguments are validated before the first launch. Returns MIXER_OK,
- * MIXER_ENOTLATIN (schedule not Latin; nothing launched), or the first layer's error.
+ * MIXER_ENOTLATIN (schedule not Latin; nothing launched), the first invalid layer's
+ * validation error (nothing launched), or MIXER_EHIP as mixer_layers_prefill reports it.
  */
 int mixer_stack_prefill(int N, const int *sched,
                         const void *const *q, const void *const *k, const void *const *v,
@@ -152,8 +156,11 @@ int mixer_stack_prefill(int N, const int *sched,
  * variants        n mixer_variant values; layer l runs variants[l].
  * q, k, v, out    host arrays of n device pointers, one [B, H, L, d] bf16 tensor each.
  * window, lambda, layer_events   as for mixer_stack_prefill (layer_events: n + 1 events).
- * Every layer's arguments are validated before the first launch. Returns MIXER_OK or the
- * first layer's error (nothing launched then).
+ * Every layer's arguments are validated before the first launch. Returns MIXER_OK, the
+ * first invalid layer's validation error (nothing launched then), or MIXER_EHIP when the
+ * runtime refuses a launch or an event record part-way: layers 0 .. l-1 before the failing
+ * one (and their events) may then already be enqueued on `stream` and will run; the
+ * caller synchronises the stream before reusing their outputs.
  */
 int mixer_layers_prefill(int n, const int *variants,
                          const void *const *q, const void *const *k, const void *const *v,

@@ -157,13 +157,3 @@ def attention_general(q, k, v, scale: float, window: int = 0, threads: int = 0):
         raise ValueError("oracle rejected arguments")
     return out
 
-
-def useful_pairs(variant, L: int, window: int = 0) -> int:
-    """Number of visible (query, key) pairs of one head, counted one row at a time."""
-    if isinstance(variant, str):
-        variant = VARIANTS[variant]
-    total = 0
-    for i in range(L):
-        lo = max(0, i - window + 1) if variant == SLIDING else 0
-        total += i - lo + 1
-    return total

@@ -14,6 +14,7 @@
 #include "mixer.h"
 
 extern std::vector<mixer::PrefillLaunch> g_launches;
+extern long g_fail_launch_at, g_launch_calls, g_fail_event_at;
 extern int g_ceiling_calls;
 extern int g_events;
 
@@ -181,6 +182,31 @@ static void test_layers() {
   CHECK(g_launches.size() == n2);
   CHECK(mixer_layers_prefill(0, periodic, q.data(), k.data(), v.data(), o.data(), 16, 0.8f, 1, 2,
                              64, 128, nullptr, nullptr) == MIXER_EINVAL);
+  // A launch the runtime refuses part-way (layer 4): MIXER_EHIP, the layers before it stay
+  // enqueued, none after it is launched.
+  ev[9] = P(109);
+  const size_t n3 = g_launches.size();
+  g_fail_launch_at = g_launch_calls + 4;
+  CHECK(mixer_stack_prefill(N, sched, q.data(), k.data(), v.data(), o.data(), 16, 0.8f, 1, 2, 64,
+                            128, nullptr, ev.data()) == MIXER_EHIP);
+  g_fail_launch_at = -1;
+  CHECK(g_launches.size() == n3 + 4);
+  for (int l = 0; l < 4 && g_launches.size() == n3 + 4; ++l)
+    CHECK(g_launches[n3 + l].q == q[l] && g_launches[n3 + l].variant == sched[l]);
+  // An event record refused after layer 2: MIXER_EHIP with layers 0..2 enqueued.
+  const size_t n4 = g_launches.size();
+  g_fail_event_at = g_events + 3;  // event 0 (before layer 0), then after layers 0, 1, 2
+  CHECK(mixer_layers_prefill(9, periodic, q.data(), k.data(), v.data(), o.data(), 16, 0.8f, 1, 2,
+                             64, 128, nullptr, ev.data()) == MIXER_EHIP);
+  g_fail_event_at = -1;
+  CHECK(g_launches.size() == n4 + 3);
+  // The single-layer call reports a refused launch as MIXER_EHIP and records nothing.
+  const size_t n5 = g_launches.size();
+  g_fail_launch_at = g_launch_calls;
+  CHECK(mixer_prefill_async(P(40), P(41), P(42), P(43), MIXER_FULL, 0, 0.f, 1, 2, 64, 128,
+                            nullptr) == MIXER_EHIP);
+  g_fail_launch_at = -1;
+  CHECK(g_launches.size() == n5);
   CHECK(mixer_stack_prefill(INT_MAX, sched, q.data(), k.data(), v.data(), o.data(), 16, 0.8f, 1,
                             2, 64, 128, nullptr, nullptr) == MIXER_EINVAL);
 }

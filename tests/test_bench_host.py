@@ -1,6 +1,7 @@
 """Host-side logic of bench.py, on the CPU: the useful-work count behind every TFLOP/s figure,
-the HBM traffic summary (counter scaling and the source hash that keys it) and the one-GPU
-guard. Nothing here touches a GPU."""
+the executed matrix-instruction count of the kernels' tile schedule, the counter summaries
+(HBM traffic, matrix-pipe busy share; counter scaling and the source hash that keys them)
+and the one-GPU guard. Nothing here touches a GPU."""
 import os
 import subprocess
 import sys
@@ -41,8 +42,71 @@ def test_useful_flops_of_the_stack_workload():
     assert sliding == 4 * 128 * 16 * (1024 * 1025 // 2 + (8192 - 1024) * 1024)
     # Three layers of each variant per step of the 3x3 square.
     assert 3 * (full + sliding + diff) == pytest.approx(1.84275e12, rel=1e-5)
-    assert bench.executed_per_useful("differential") == 1.5
-    assert bench.executed_per_useful("full") == bench.executed_per_useful("sliding") == 1.0
+
+
+def test_executed_mfmas_closed_forms():
+    # Full at B=1, H=16, L=8192 (64 query tiles of 128 rows, one wave per row block): query
+    # tile t spans key tiles 0..2t+1, and each of its 4 waves issues 32 MFMAs per tile
+    # (scores 16 + value product 16, the first iteration's value product on zeros standing
+    # in for the one before the first tile); the last tile's value product after the loop
+    # adds 16 for the waves of the last 64 rows, the only ones that see that tile.
+    per_head = sum(4 * 32 * (2 * t + 2) + 2 * 16 for t in range(64))
+    assert bench.executed_mfmas("full", 1, 16, 8192, 128, 0) == 16 * per_head
+    # Differential: 8 waves, hi + 2 matrix phases of 8 + 16 MFMAs each, hi = 2t + 1.
+    per_head = sum(8 * (2 * t + 3) * 24 for t in range(64))
+    assert bench.executed_mfmas("differential", 1, 16, 8192, 128, 0) == 16 * per_head
+    # Sliding, W = 1024, a query tile past the first window: 18 key tiles, every wave all of
+    # them (one wave per row block keeps the first scores and the last value product).
+    full_tiles = 4 * (32 * 18 + 16)
+    assert bench.executed_mfmas("sliding", 1, 1, 2048, 128, 1024, n_cu=0) - \
+        bench.executed_mfmas("sliding", 1, 1, 1920, 128, 1024, n_cu=0) == full_tiles
+
+
+@pytest.mark.parametrize("variant,L,W", [("full", 1, 0), ("full", 300, 0), ("full", 2048, 0),
+                                         ("sliding", 777, 100), ("sliding", 8192, 1024),
+                                         ("differential", 129, 0), ("differential", 4096, 0)])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n_cu", [0, 256])
+def test_executed_mfmas_cover_the_useful_work(variant, L, W, d, n_cu):
+    # Whole tiles and masked keys: never less matrix work than the useful flops, and the
+    # differential's second value product makes it at least 1.5 times the useful work.
+    ex = bench.executed_mfmas(variant, 1, 4, L, d, W, n_cu=n_cu) * bench.MFMA_FLOPS
+    fl = bench.useful_flops(variant, 1, 4, L, d, W)
+    assert ex >= (1.5 if variant == "differential" else 1.0) * fl
+
+
+def test_executed_mfmas_match_the_committed_counters():
+    # The instruction counter of the committed SQ summary (taken on the bench's stack) is
+    # the same count, exactly, while the summary describes the current kernel source.
+    for v in bench.VARIANT_NAMES:
+        sq = bench.read_sq(v)
+        if sq is None:
+            pytest.skip("no SQ summary for the current kernel source")
+        w = 1024 if v == "sliding" else 0
+        assert sq["sq_insts_mfma"] == bench.executed_mfmas(v, 1, 16, 8192, 128, w)
+
+
+def test_write_sq_reads_busy_share_and_clock(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "SQ_FILE", str(tmp_path / "sq_busy.txt"))
+    path = tmp_path / "c.csv"
+    name = "_ZN5mixer3dma18prefill_dma_kernelILi128ELi0ELi1EEEvPKDF16b"
+    with open(path, "w") as f:
+        f.write('"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value",'
+                '"Start_Timestamp","End_Timestamp"\n')
+        for did, busy, grbm in ((1, 1024 * 500, 8 * 1000), (2, 1024 * 600, 8 * 1000)):
+            for cn, cv in (("SQ_VALU_MFMA_BUSY_CYCLES", busy), ("SQ_INSTS_MFMA", 77),
+                           ("GRBM_GUI_ACTIVE", grbm)):
+                f.write(f'{did},"{name}","{cn}",{cv},1000,1500\n')
+    bench.write_sq(str(path), "test")
+    sq = bench.read_sq("full")
+    assert sq["mfma_busy"] == pytest.approx(0.55)        # (500 + 600) / 2 / 1000
+    assert sq["sq_insts_mfma"] == 77
+    assert sq["effective_clock_ghz"] == pytest.approx(2.0)  # 1000 cycles in 500 ns
+    assert bench.read_sq("sliding") is None
+
+
+def test_cpu_model_is_named():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
 
 
 def test_code_only_ignores_comments_and_layout():

@@ -68,7 +68,10 @@ ARMS = {
 
 
 @pytest.mark.parametrize("arm", sorted(ARMS))
-def test_layers_runner_runs_every_arm_as_its_layers(arm):
+def test_layers_runner_runs_every_arm_as_its_layers(oracle_mod, arm):
+    """Every arm through mixer_layers_prefill: each layer bitwise equal to the same layer
+    launched alone, and the first layer of each type in the arm against the oracle on
+    sampled rows of every head."""
     import torch
     B, H, L, d, W, lam = 1, 4, 300, 128, 100, 0.8
     variants = ARMS[arm]
@@ -80,6 +83,12 @@ def test_layers_runner_runs_every_arm_as_its_layers(arm):
     for i, (t, o) in enumerate(zip(layers, outs)):
         ref = run_layer(t, NAMES[variants[i]], W, lam)
         assert torch.equal(o, ref), f"{arm} layer {i}"
+    rows = sample_rows(L, seed=3, n_random=40, edge=12)
+    for vt in sorted(set(variants)):
+        i = variants.index(vt)
+        inp = make(700 + i, B, H, L, d)
+        ref = oracle_mod.prefill_rows(inp.q, inp.k, inp.v, NAMES[vt], W, lam, rows)
+        assert_close(to_f64(outs[i][:, :, rows]), ref, f"{arm} layer {i} ({NAMES[vt]})")
 
 
 def test_bench_stack_at_full_size_against_the_oracle(oracle_mod):
