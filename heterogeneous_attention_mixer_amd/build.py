@@ -5,6 +5,7 @@ Usage: ``python -m heterogeneous_attention_mixer_amd.build`` (always recompiles)
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 import tempfile
@@ -30,7 +31,30 @@ FLAGS = [
 # value it uses), which lets fmaxf chains become plain v_max3_f32; the host API, whose
 # argument checks test for NaN, keeps IEEE semantics.
 SOURCE_FLAGS = {"attn_prefill_dma.hip": ["-fno-honor-nans"]}
+# Sources whose kernels must build with no register spills and no scratch: their key loops
+# issue tile loads the compiler does not track and wait on them with counted waits, which a
+# spill (a counted scratch access) inside the loop would break. The compiler's resource
+# remarks are read for them on every build.
+NO_SPILL = ("attn_prefill_dma.hip",)
+RESOURCE_REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
 NOISE = "is not a recognized feature for this target"
+
+
+def spilling_kernels(remarks: str) -> list:
+    """(kernel, what) for every kernel whose resource remarks report a register spill or a
+    non-zero scratch size."""
+    bad = []
+    name = None
+    for line in remarks.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+(VGPRs Spill|SGPRs Spill|ScratchSize \[bytes/lane\]): (\d+)",
+                      line)
+        if m and name and int(m.group(2)) != 0:
+            bad.append((name, f"{m.group(1)} {m.group(2)}"))
+    return bad
 
 
 def _run(cmd, verbose):
@@ -40,8 +64,11 @@ def _run(cmd, verbose):
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if NOISE not in ln]
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    remarks = [ln for ln in msgs if "kernel-resource-usage" in ln]
+    msgs = [ln for ln in msgs if "kernel-resource-usage" not in ln]
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
+    return "\n".join(remarks)
 
 
 def build(extra_flags=None, out: str = LIB, verbose: bool = False) -> str:
@@ -50,9 +77,16 @@ def build(extra_flags=None, out: str = LIB, verbose: bool = False) -> str:
     objs = []
     with tempfile.TemporaryDirectory(prefix="mixer_build_") as tmpdir:
         for src in SOURCES:
-            obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
-            _run([HIPCC, *FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []),
-                  *(extra_flags or []), "-c", src, "-o", obj], verbose)
+            base = os.path.basename(src)
+            obj = os.path.join(tmpdir, base + ".o")
+            remarks = _run([HIPCC, *FLAGS, *SOURCE_FLAGS.get(base, []),
+                            *(RESOURCE_REMARKS if base in NO_SPILL else []),
+                            *(extra_flags or []), "-c", src, "-o", obj], verbose)
+            if base in NO_SPILL:
+                bad = spilling_kernels(remarks)
+                if bad:
+                    raise RuntimeError(f"{base}: kernels spill or use scratch, which the "
+                                       f"untracked tile loads do not allow: {bad}")
             objs.append(obj)
         tmp = out + ".tmp"
         _run([HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", tmp], verbose)
