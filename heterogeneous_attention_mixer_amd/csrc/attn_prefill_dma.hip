@@ -43,8 +43,8 @@
 //     phase takes the exponentials against the current reference and leaves the row max to
 //     a rare path at the start of the next matrix phase, taken only while a row has no
 //     reference or when the lane's tile sum exceeds 2^8.
-//   * Work order: heaviest query tiles first; all tiles of a head on one XCD when B*H is a
-//     multiple of 8.
+//   * Work order: heaviest query tiles first (sliding: the short first-window tiles first);
+//     all tiles of a head on one XCD when B*H is a multiple of 8.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -187,7 +187,7 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   const int lg = lane >> 5;
 
   int bh, qt;
-  map_unit(blockIdx.x, BH, nq, &bh, &qt);
+  map_unit(blockIdx.x, BH, nq, &bh, &qt, kSlide);
   const int q0 = qt * BM;
   const int qw = q0 + rb * 32;
   const int qi = qw + lr;

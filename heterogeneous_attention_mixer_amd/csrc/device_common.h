@@ -98,19 +98,27 @@ __device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// (batch*head, query tile) of workgroup `bid`: heaviest query tiles first. Workgroups are
-// dealt to the 8 XCDs round-robin; when the head count is a multiple of 8, XCD (bid mod 8)
-// takes a contiguous block of BH/8 heads, all their query tiles, so that a head's K/V (and
-// that of query heads sharing one K/V head) is served from one L2.
-__device__ __forceinline__ void map_unit(int bid, int BH, int nq, int* bh, int* qt) {
+// (batch*head, query tile) of workgroup `bid`. Workgroups are dealt to the 8 XCDs
+// round-robin; when the head count is a multiple of 8, XCD (bid mod 8) takes a contiguous
+// block of BH/8 heads, all their query tiles, so that a head's K/V (and that of query heads
+// sharing one K/V head) is served from one L2.
+// Causal layers go heaviest query tile first (the last tiles see the most keys), so that
+// the light tiles fill the end. With `ascending` (the sliding window, where every tile past
+// the first window costs the same) the short first-window tiles go first: the two
+// workgroups that share a CU then start and end at different times, and one's prologue and
+// epilogue overlap the other's key loop instead of coinciding with it.
+__device__ __forceinline__ void map_unit(int bid, int BH, int nq, int* bh, int* qt,
+                                         bool ascending = false) {
+  int rank;
   if ((BH & 7) == 0) {
     const int x = bid & 7, j = bid >> 3, hpx = BH >> 3;
-    *qt = nq - 1 - j / hpx;
+    rank = j / hpx;
     *bh = x * hpx + j % hpx;
   } else {
     *bh = bid % BH;
-    *qt = nq - 1 - bid / BH;
+    rank = bid / BH;
   }
+  *qt = ascending ? rank : nq - 1 - rank;
 }
 
 }  // namespace mixer

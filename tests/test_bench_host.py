@@ -145,6 +145,50 @@ def test_write_traffic_scales_by_the_copy_and_reads_back(tmp_path, monkeypatch):
     assert bench.read_traffic("sliding") is None  # no counters for it
 
 
+def test_launch_threads_follow_the_launcher():
+    # 128-row query tiles; 4 waves per full/sliding workgroup, 8 with the key split (at most
+    # one workgroup per CU) and for the differential. The profiler reported these Grid_Size
+    # values for the bench's launches.
+    assert bench.launch_threads("full", 1, 16, 8192) == 262144
+    assert bench.launch_threads("sliding", 1, 16, 8192) == 262144
+    assert bench.launch_threads("differential", 1, 16, 8192) == 524288
+    assert bench.launch_threads("full", 1, 16, 2048) == 131072       # key split
+    assert bench.launch_threads("full", 1, 16, 32768) == 1048576
+    assert bench.launch_threads("differential", 1, 16, 32768) == 2097152
+    assert bench.launch_threads("full", 1, 1, 300) == 3 * 512
+
+
+def test_counter_summaries_take_the_stack_launches_only(tmp_path, monkeypatch):
+    # A run that also times other lengths: launches of the same kernel with another grid
+    # stay out of the per-launch averages.
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "hbm_traffic.txt"))
+    monkeypatch.setattr(bench, "SQ_FILE", str(tmp_path / "sq_busy.txt"))
+    name = "_ZN5mixer3dma18prefill_dma_kernelILi128ELi0ELi1EEEvPKDF16b"
+    stack, other = bench.launch_threads("full", 1, 16, 8192), bench.launch_threads(
+        "full", 1, 16, 32768)
+    mib = 1024
+    for counter, copy_kib, kib in (("FETCH_SIZE", 256 * mib, (10 * mib, 999 * mib)),
+                                   ("WRITE_SIZE", 256 * mib, (4 * mib, 99 * mib))):
+        with open(tmp_path / f"{counter}.csv", "w") as f:
+            f.write('"Dispatch_Id","Grid_Size","Kernel_Name","Counter_Name","Counter_Value"\n')
+            f.write(f'1,131072,"__amd_rocclr_copyBuffer","{counter}",{copy_kib}\n')
+            f.write(f'2,{stack},"{name}","{counter}",{kib[0]}\n')
+            f.write(f'3,{other},"{name}","{counter}",{kib[1]}\n')
+    bench.write_traffic(str(tmp_path / "FETCH_SIZE.csv"), str(tmp_path / "WRITE_SIZE.csv"),
+                        "test")
+    assert bench.read_traffic("full") == pytest.approx(14 * 1024 * 1024)
+    with open(tmp_path / "sq.csv", "w") as f:
+        f.write('"Dispatch_Id","Grid_Size","Kernel_Name","Counter_Name","Counter_Value",'
+                '"Start_Timestamp","End_Timestamp"\n')
+        for did, grid, busy in ((1, stack, 1024 * 500), (2, other, 1024 * 900)):
+            for cn, cv in (("SQ_VALU_MFMA_BUSY_CYCLES", busy), ("SQ_INSTS_MFMA", did),
+                           ("GRBM_GUI_ACTIVE", 8 * 1000)):
+                f.write(f'{did},{grid},"{name}","{cn}",{cv},1000,1500\n')
+    bench.write_sq(str(tmp_path / "sq.csv"), "test")
+    sq = bench.read_sq("full")
+    assert sq["mfma_busy"] == pytest.approx(0.5) and sq["sq_insts_mfma"] == 1
+
+
 def test_traffic_is_dropped_when_the_kernel_source_changes(tmp_path, monkeypatch):
     path = tmp_path / "hbm_traffic.txt"
     path.write_text("kernel_source_sha256_16 = 0000000000000000\n"
