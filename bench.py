@@ -65,7 +65,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 SQ_FILE = os.path.join(ROOT, "profiles", "sq_busy.txt")
 # MI355X: 8 XCDs of 32 CUs, 4 SIMDs per CU.
 N_XCD, N_CU, N_SIMD = 8, 256, 1024
-MFMA_FLOPS = 32 * 32 * 16 * 2  # one v_mfma_f32_32x32x16_bf16
+MFMA_FLOPS = 32 * 32 * 16 * 2    # one v_mfma_f32_32x32x16_bf16 (scores, value products)
+MFMA16_FLOPS = 16 * 16 * 32 * 2  # one v_mfma_f32_16x16x32_bf16 (the differential's row sums)
 # Sources of the bf16 kernel the bench times (a traffic summary is valid only for them).
 KERNEL_SOURCES = [os.path.join(ROOT, "heterogeneous_attention_mixer_amd", "csrc", f)
                   for f in ("attn_prefill_dma.hip", "device_common.h", "kernels.h")]
@@ -90,10 +91,10 @@ def useful_flops(variant: str, B: int, H: int, L: int, d: int, window: int) -> i
     return 4 * d * B * H * visible_pairs(variant, L, window)
 
 
-def executed_mfmas(variant: str, B: int, H: int, L: int, d: int, window: int,
-                   n_cu: int = N_CU) -> int:
-    """Matrix instructions (v_mfma_f32_32x32x16_bf16) one launch of the bf16 kernel issues,
-    counted from the same tile schedule the kernels follow: whole 64-key tiles, 32 query rows
+def executed_mfma_split(variant: str, B: int, H: int, L: int, d: int, window: int,
+                        n_cu: int = N_CU):
+    """Matrix instructions one launch of the bf16 kernel issues, as (32x32x16, 16x16x32)
+    counts, from the same tile schedule the kernels follow: whole 64-key tiles, 32 query rows
     per wave, masked keys computed like visible ones.
 
     Full and sliding (128 query rows per workgroup, 4 row blocks): per wave, the scores of
@@ -105,7 +106,11 @@ def executed_mfmas(variant: str, B: int, H: int, L: int, d: int, window: int,
     the first scores of a tile no row of it sees and the last value product of a tile past
     its rows, where the kernel does (see the kernel's prologue and tail).
     Differential (8 waves: 4 row blocks x 2 maps): per wave hi + 2 matrix phases of the
-    half-width scores and the full-width value product each."""
+    half-width scores and the full-width value product each, and four 16x16x32 row-sum
+    instructions per exponential pass: one per vector phase (hi + 1) and one more for the
+    first tile, which is taken again once its rows have a reference. Passes taken again
+    because a tile's sum exceeds 2^8 depend on the data and are not counted (none on the
+    bench's inputs)."""
     bm, bn = 128, 64
     nq = (L + bm - 1) // bm
     qk = 2 * (d // 16)          # one tile's scores: 2 key blocks x d/16 steps
@@ -114,10 +119,12 @@ def executed_mfmas(variant: str, B: int, H: int, L: int, d: int, window: int,
     total = 0
     if variant == "differential":
         qk_half = 2 * (d // 32)
+        small = 0
         for qt in range(nq):
             hi = (min(qt * bm + bm, L) - 1) // bn
             total += 8 * (hi + 2) * (qk_half + pv)
-        return B * H * total
+            small += 8 * (hi + 2) * 4
+        return B * H * total, B * H * small
     spl = 2 if B * H * nq <= n_cu else 1
     for qt in range(nq):
         q0 = qt * bm
@@ -135,7 +142,21 @@ def executed_mfmas(variant: str, B: int, H: int, L: int, d: int, window: int,
                 tail = (slide and spl == 1) or jl * bn <= qw + 31
                 total += (qk if see_first else 0) + (n_it - 1) * (qk + pv) + pv + \
                     (pv if tail else 0)
-    return B * H * total
+    return B * H * total, 0
+
+
+def executed_mfmas(variant: str, B: int, H: int, L: int, d: int, window: int,
+                   n_cu: int = N_CU) -> int:
+    """Matrix instructions of one launch (what SQ_INSTS_MFMA counts); see
+    executed_mfma_split."""
+    return sum(executed_mfma_split(variant, B, H, L, d, window, n_cu))
+
+
+def executed_flops(variant: str, B: int, H: int, L: int, d: int, window: int,
+                   n_cu: int = N_CU) -> int:
+    """Flops of the matrix instructions of one launch; see executed_mfma_split."""
+    n32, n16 = executed_mfma_split(variant, B, H, L, d, window, n_cu)
+    return n32 * MFMA_FLOPS + n16 * MFMA16_FLOPS
 
 
 def launch_threads(variant: str, B: int, H: int, L: int, n_cu: int = N_CU) -> int:
@@ -522,7 +543,7 @@ def main(argv=None) -> int:
             continue
         ms = sum(ts) / len(ts)
         fl = useful_flops(name, B, H, L, d, W)
-        ex = executed_mfmas(name, B, H, L, d, W) * MFMA_FLOPS
+        ex = executed_flops(name, B, H, L, d, W)
         srt = sorted(ts)
         per_variant[name] = {
             "ms_per_launch": round(ms, 5),
@@ -690,20 +711,20 @@ def main(argv=None) -> int:
                 o = torch.empty_like(t[0])
                 settle(lambda: mixer.mixer_prefill_async(*t, o, variant, 0, lam),
                        args.settle)
-                # One call of the layers runner enqueues every repetition, so that a short
-                # kernel (34 us at L=2048) is not left waiting for the Python binding's
-                # per-call work between launches.
+                # One call of the layers runner enqueues every repetition, and the library
+                # records the events around them on the launch stream, so that a short kernel
+                # (34 us at L=2048) waits neither for the Python binding's per-call work
+                # between launches nor for its argument setup before the first.
                 reps = 10 if Lx <= 8192 else 3
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
+                evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+                for e in evs:
+                    e.record()  # creates the events; the library re-records them
                 mixer.mixer_layers_prefill([variant] * reps, [t[0]] * reps, [t[1]] * reps,
-                                           [t[2]] * reps, [o] * reps, 0, lam)
-                e1.record()
+                                           [t[2]] * reps, [o] * reps, 0, lam, events=evs)
                 torch.cuda.synchronize()
-                ms = e0.elapsed_time(e1) / reps
+                ms = evs[0].elapsed_time(evs[-1]) / reps
                 fl = useful_flops(variant, B, H, Lx, d, 0)
-                ex = executed_mfmas(variant, B, H, Lx, d, 0) * MFMA_FLOPS
+                ex = executed_flops(variant, B, H, Lx, d, 0)
                 sweep[f"{name}_L{Lx}"] = {
                     "ms_per_launch": round(ms, 5),
                     "useful_tflops": round(fl / (ms * 1e-3) / 1e12, 2),

@@ -35,7 +35,8 @@
 //   * Online softmax in fp32 with exp2 (scale folded with log2 e); the reference max moves
 //     only when a score beats it by more than 2^8 (probabilities stay below 256), so the
 //     accumulator rescale is rare. Row sums are taken over the bf16-rounded probabilities,
-//     the exact weights of the value product.
+//     the exact weights of the value product: by v_dot2 in the pipelined kernel, by four
+//     small MFMAs per tile in the differential's (whose registers leave room for them).
 //   * The differential runs its own kernel (prefill_diff_kernel, below): each softmax map
 //     gets its own wave (scores on its half of the head dim, values on all of it), and the
 //     two waves of a row block, which share a SIMD, alternate between a matrix phase and a
@@ -589,9 +590,9 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
 // head dim and the value product over all of it; the two maps of a row block meet once, at
 // the end, through LDS. The map-1 waves run one phase behind the map-0 waves. Per key tile
 // k a wave runs an M phase (matrix work only: S[k] = K[k] Q^T, then O += V[k-1] P[k-1]) and
-// a V phase (vector work only: the exponentials of S[k] into P[k] against the current
-// reference, their sum in four independent partial sums, and the loads of later tiles). The
-// reference test for tile k (no reference yet, or a lane's tile sum above 2^8: then the row
+// a V phase (vector work: the exponentials of S[k] into P[k] against the current
+// reference, the loads of later tiles, and four small MFMAs for the row sums of P[k]). The
+// reference test for tile k (no reference yet, or a row's tile sum above 2^8: then the row
 // max, the move with l and O, and the exponentials again) runs at the start of the M phase
 // of tile k+1, before S is overwritten; it is rare. So on every SIMD one wave feeds the matrix
 // core while its partner does the softmax, and a barrier ends every phase. The M phase runs
@@ -709,7 +710,22 @@ prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   float m = -INFINITY, l = 0.0f;
-  float lt = 0.0f;  // this lane's sum of the last tile's probabilities, not yet in l
+  float lt = 0.0f;  // the row's sum of the last tile's probabilities, not yet in l
+  // Row sums on the matrix core: v_mfma_f32_16x16x32_bf16 with a 0/1 selector as A and a
+  // probability register as B. As B, lane l's register is k-group l/16 of column l%16; it
+  // holds 8 probabilities of query l%32, so query n (< 16) fills k-groups 0 and 2 of column
+  // n and query n+16 k-groups 1 and 3. Selector rows 0 and 8 take k-groups 0 and 2, rows 4
+  // and 12 take 1 and 3, and the result's element 0 in lane l is row 4*(l/16) of column
+  // l%16: the whole row sum of query l%32, in both lanes of the query. Four of these
+  // (16 cycles each on the matrix pipe) replace 16 v_dot2c, each of which holds the matrix
+  // pipe for about 10 cycles, out of the vector phase that runs beside the partner's MFMAs.
+  bf16x8 rsel;
+  {
+    const int sr = lane & 15, sg = (lane >> 4) & 1;
+    const bool one = ((sr == 0 || sr == 8) && sg == 0) || ((sr == 4 || sr == 12) && sg == 1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rsel[e] = one ? (__bf16)1.0f : (__bf16)0.0f;
+  }
   floatx16 s[2];
   bf16x8 p[2][2];
 #pragma unroll
@@ -720,31 +736,26 @@ prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg
       for (int e = 0; e < 8; ++e) p[kb][h][e] = (__bf16)0.0f;
 
   // Probabilities exp2(c (s - m)) of the tile against the current reference, rounded to
-  // bf16 into p; their sum into lt, over four independent partial sums (one per 16-key
-  // group), so that no 16-long chain of dependent additions sits in the V phase.
+  // bf16 into p; the row's sum of the rounded values into lt, on the matrix core.
   auto take_exps = [&]() {
     const float mc = (m == -INFINITY) ? 0.0f : m * c;
-    bf16x2 ones;
-    ones[0] = (__bf16)1.0f;
-    ones[1] = (__bf16)1.0f;
-    float ls[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          bf16x2 q2;
-          q2[0] = (__bf16)fast_exp2(__builtin_fmaf(s[kb][h * 8 + e], c, -mc));
-          q2[1] = (__bf16)fast_exp2(__builtin_fmaf(s[kb][h * 8 + e + 1], c, -mc));
-          p[kb][h][e] = q2[0];
-          p[kb][h][e + 1] = q2[1];
-          ls[kb][h] = __builtin_amdgcn_fdot2_f32_bf16(q2, ones, ls[kb][h], false);
-        }
-    lt = (ls[0][0] + ls[0][1]) + (ls[1][0] + ls[1][1]);
+        for (int e = 0; e < 8; ++e)
+          p[kb][h][e] = (__bf16)fast_exp2(__builtin_fmaf(s[kb][h * 8 + e], c, -mc));
+    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rsel, p[kb][h], acc, 0, 0, 0);
+    lt = acc[0];
   };
   // Reference test for the tile whose probabilities the V phase just took (S still holds
-  // its masked scores). While a row has no reference yet, or when a lane's tile sum says a
+  // its masked scores). While a row has no reference yet, or when a row's tile sum says a
   // probability may exceed 2^gap, the row max moves the reference, l and O follow (O holds
   // the tiles before this one), and the probabilities are taken again. Then l takes lt.
   auto settle = [&]() {
@@ -837,8 +848,6 @@ prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg
           if (kb * 32 + 8 * (r >> 2) + (r & 3) > t) s[kb][r] = -INFINITY;
     }
     take_exps();
-    // lt is read only at the start of the next M phase: keep its sums in this phase.
-    asm volatile("" : "+v"(lt));
   };
 
   // ---- prologue (lo is tile 0): pair 0 = (K[0], zeros), pair 1 = (K[1], V[0]),
@@ -875,7 +884,7 @@ prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg
 
   // ---- epilogue: out = O1 / l1 - lambda * O2 / l2, map 1's term passed to map 0 through
   // LDS. Element (db, r) of a lane is channel db*32 + 8*(r/4) + 4*lg + r%4 of query qi.
-  const float lsum = xhalf_sum(l);
+  const float lsum = l;  // the row-sum MFMAs already add the two lanes of a query
   __syncthreads();  // every wave is done reading the tiles
   {
     float* const xch = reinterpret_cast<float*>(smem) + rb * 64 * (DB * 16);

@@ -18,7 +18,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // The reference max moves only when a score beats it by more than this many powers of two.
 constexpr float kRescaleLog2Gap = 8.0f;
 // 2^kRescaleLog2Gap: where the exponentials are taken before the reference is checked, a
-// lane's sum over one tile above this bound (which any probability above it forces) sends
+// row's sum over one tile above this bound (which any probability above it forces) sends
 // the tile back for a reference move.
 constexpr float kTileSumBound = 256.0f;
 // s_waitcnt immediate (gfx9 encoding): vmcnt = 0, expcnt and lgkmcnt left at their maxima.

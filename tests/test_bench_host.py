@@ -52,9 +52,15 @@ def test_executed_mfmas_closed_forms():
     # adds 16 for the waves of the last 64 rows, the only ones that see that tile.
     per_head = sum(4 * 32 * (2 * t + 2) + 2 * 16 for t in range(64))
     assert bench.executed_mfmas("full", 1, 16, 8192, 128, 0) == 16 * per_head
-    # Differential: 8 waves, hi + 2 matrix phases of 8 + 16 MFMAs each, hi = 2t + 1.
+    # Differential: 8 waves, hi + 2 matrix phases of 8 + 16 MFMAs each, hi = 2t + 1, and 4
+    # row-sum instructions (16x16x32) per exponential pass, hi + 2 passes.
     per_head = sum(8 * (2 * t + 3) * 24 for t in range(64))
-    assert bench.executed_mfmas("differential", 1, 16, 8192, 128, 0) == 16 * per_head
+    small = sum(8 * (2 * t + 3) * 4 for t in range(64))
+    assert bench.executed_mfma_split("differential", 1, 16, 8192, 128, 0) == (
+        16 * per_head, 16 * small)
+    assert bench.executed_mfmas("differential", 1, 16, 8192, 128, 0) == 16 * (per_head + small)
+    assert bench.executed_flops("differential", 1, 16, 8192, 128, 0) == 16 * (
+        per_head * 32768 + small * 16384)
     # Sliding, W = 1024, a query tile past the first window: 18 key tiles, every wave all of
     # them (one wave per row block keeps the first scores and the last value product).
     full_tiles = 4 * (32 * 18 + 16)
@@ -70,7 +76,7 @@ def test_executed_mfmas_closed_forms():
 def test_executed_mfmas_cover_the_useful_work(variant, L, W, d, n_cu):
     # Whole tiles and masked keys: never less matrix work than the useful flops, and the
     # differential's second value product makes it at least 1.5 times the useful work.
-    ex = bench.executed_mfmas(variant, 1, 4, L, d, W, n_cu=n_cu) * bench.MFMA_FLOPS
+    ex = bench.executed_flops(variant, 1, 4, L, d, W, n_cu=n_cu)
     fl = bench.useful_flops(variant, 1, 4, L, d, W)
     assert ex >= (1.5 if variant == "differential" else 1.0) * fl
 
