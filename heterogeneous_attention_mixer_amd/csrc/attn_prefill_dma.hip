@@ -746,12 +746,17 @@ prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           p[kb][h][e] = (__bf16)fast_exp2(__builtin_fmaf(s[kb][h * 8 + e], c, -mc));
+    // The partner wave is in its M phase at raised priority, so at the base priority these
+    // four would wait for gaps in its matrix stream (about 240 cycles of the V phase): they
+    // take the same priority and interleave with it instead.
     floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rsel, p[kb][h], acc, 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
     lt = acc[0];
   };
   // Reference test for the tile whose probabilities the V phase just took (S still holds
@@ -821,15 +826,25 @@ prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg
               bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
           o[db] = mfma32(a, p[kb][h], o[db]);
         }
-    // Operand reads a few instructions ahead of the matrix instructions that use them.
+    // Operand reads ahead of the matrix instructions that use them. A score MFMA reads one
+    // K operand, a value MFMA two V reads: three reads after each score MFMA put the value
+    // product's reads about ten MFMAs ahead when it starts, and one read after each of its
+    // first value MFMAs keeps them ahead to the end of the phase (an even 1.5 reads per
+    // MFMA let the lead fall to one MFMA, less than the LDS latency).
+    constexpr int kLate = 2 * NQ + 8 * DB - 4 - 6 * NQ;  // reads left for the value MFMAs
+    static_assert(kLate >= 0 && kLate <= 4 * DB, "read schedule");
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < (DB * 4 + 2 * NQ) / 2; ++i) {
+    for (int i = 0; i < 2 * NQ; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kLate; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * DB - kLate, 0);
   };
   // V phase of tile k: loads of pair k+3, then the probabilities of S (masked on tiles
   // that cross the diagonal) against the current reference.
