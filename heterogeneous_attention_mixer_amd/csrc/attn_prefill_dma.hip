@@ -43,7 +43,7 @@
 //     vector phase one phase apart; they meet once, at the end, through LDS. Its vector
 //     phase takes the exponentials against the current reference and leaves the row max to
 //     a rare path at the start of the next matrix phase, taken only while a row has no
-//     reference or when the lane's tile sum exceeds 2^8.
+//     reference or when a row's tile sum exceeds 2^8.
 //   * Work order: heaviest query tiles first (sliding: the short first-window tiles first);
 //     all tiles of a head on one XCD when B*H is a multiple of 8.
 #include <hip/hip_runtime.h>

@@ -106,7 +106,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // the light tiles fill the end. With `ascending` (the sliding window, where every tile past
 // the first window costs the same) the short first-window tiles go first: the two
 // workgroups that share a CU then start and end at different times, and one's prologue and
-// epilogue overlap the other's key loop instead of coinciding with it.
+// epilogue overlap the other's key loop instead of coinciding with it. The workgroups in
+// flight on an XCD then also hold neighbouring query tiles, whose windows share all but a
+// few K/V tiles, so each K/V tile comes from HBM about once.
 __device__ __forceinline__ void map_unit(int bid, int BH, int nq, int* bh, int* qt,
                                          bool ascending = false) {
   int rank;
