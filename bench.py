@@ -72,9 +72,16 @@ KERNEL_SOURCES = [os.path.join(ROOT, "heterogeneous_attention_mixer_amd", "csrc"
                   for f in ("attn_prefill_dma.hip", "device_common.h", "kernels.h")]
 # The d=128 bf16 kernel of each variant: its name as reported, and a substring of its
 # mangled symbol in profiler output.
-KERNELS = {"full": ("prefill_dma_kernel<128, full>", "prefill_dma_kernelILi128ELi0E"),
+KERNELS = {"full": ("prefill_phase_kernel<128, full>", "prefill_phase_kernelILi128ELi0E"),
            "sliding": ("prefill_dma_kernel<128, sliding>", "prefill_dma_kernelILi128ELi1E"),
-           "differential": ("prefill_diff_kernel<128>", "prefill_diff_kernelILi128EE")}
+           "differential": ("prefill_phase_kernel<128, differential>",
+                            "prefill_phase_kernelILi128ELi2E")}
+
+
+def full_takes_phase_kernel(B: int, H: int, L: int, n_cu: int = N_CU) -> bool:
+    """Whether a full causal layer runs the phase-separated kernel (256-row workgroups): when
+    its grid holds more than one of them per CU, as the launcher decides."""
+    return B * H * ((L + 255) // 256) > n_cu
 
 
 def visible_pairs(variant: str, L: int, window: int) -> int:
@@ -105,24 +112,26 @@ def executed_mfma_split(variant: str, B: int, H: int, L: int, d: int, window: in
     waves per row block, alternate tiles); otherwise one wave per row block. A wave skips
     the first scores of a tile no row of it sees and the last value product of a tile past
     its rows, where the kernel does (see the kernel's prologue and tail).
-    Differential (8 waves: 4 row blocks x 2 maps): per wave hi + 2 matrix phases of the
-    half-width scores and the full-width value product each, and four 16x16x32 row-sum
-    instructions per exponential pass: one per vector phase (hi + 1) and one more for the
-    first tile, which is taken again once its rows have a reference. Passes taken again
-    because a tile's sum exceeds 2^8 depend on the data and are not counted (none on the
-    bench's inputs)."""
+    Phase-separated kernel, the differential (8 waves: 4 row blocks x 2 maps, 128 rows) and
+    full causal on grids of more than one 256-row workgroup per CU (8 waves: 8 row blocks):
+    per wave hi + 2 matrix phases of the scores (half-width for the differential) and the
+    value product each, and four 16x16x32 row-sum instructions per exponential pass: one
+    per vector phase (hi + 1) and one more for the first tile, which is taken again once
+    its rows have a reference. Passes taken again because a tile's sum exceeds 2^8 depend
+    on the data and are not counted (none on the bench's inputs)."""
     bm, bn = 128, 64
     nq = (L + bm - 1) // bm
     qk = 2 * (d // 16)          # one tile's scores: 2 key blocks x d/16 steps
     pv = 2 * 2 * (d // 32)      # one tile's value product: 4 key groups x d/32 channel blocks
     slide = variant == "sliding"
     total = 0
-    if variant == "differential":
-        qk_half = 2 * (d // 32)
+    if variant == "differential" or (variant == "full" and
+                                     full_takes_phase_kernel(B, H, L, n_cu)):
+        rows, qk_phase = (128, 2 * (d // 32)) if variant == "differential" else (256, qk)
         small = 0
-        for qt in range(nq):
-            hi = (min(qt * bm + bm, L) - 1) // bn
-            total += 8 * (hi + 2) * (qk_half + pv)
+        for qt in range((L + rows - 1) // rows):
+            hi = (min(qt * rows + rows, L) - 1) // bn
+            total += 8 * (hi + 2) * (qk_phase + pv)
             small += 8 * (hi + 2) * 4
         return B * H * total, B * H * small
     spl = 2 if B * H * nq <= n_cu else 1
@@ -163,7 +172,10 @@ def launch_threads(variant: str, B: int, H: int, L: int, n_cu: int = N_CU) -> in
     """Work-items in one launch of the d=128 bf16 kernel (the Grid_Size profilers report):
     one workgroup per (b*h, 128-row query tile); 256 work-items per full/sliding workgroup,
     512 with the key split (grids of at most one workgroup per CU) and for the
-    differential."""
+    differential; full on the phase-separated kernel, one 512-item workgroup per 256-row
+    query tile."""
+    if variant == "full" and full_takes_phase_kernel(B, H, L, n_cu):
+        return B * H * ((L + 255) // 256) * 512
     wgs = B * H * ((L + 127) // 128)
     if variant == "differential" or wgs <= n_cu:
         return wgs * 512

@@ -1,6 +1,7 @@
 // attn_prefill_dma.hip -- bf16 causal prefill of one sequence-mixer layer for gfx950, with
-// K/V tiles moved HBM -> LDS by the buffer unit (no register staging) and a software
-// pipeline that overlaps each tile's softmax with the matrix products of its neighbours.
+// K/V tiles moved HBM -> LDS by the buffer unit (no register staging) and the softmax of
+// each tile overlapped with matrix products: within a wave (the pipelined kernel) or between
+// the two waves of a SIMD (the phase-separated kernel).
 //
 // Variants (Table 1, sec. 3.1 of "Placement Is Free, Composition Is Not: The Latin Square as
 // a Provably-Balanced Construction for Heterogeneous Sequence-Mixer Stacks"):
@@ -25,7 +26,8 @@
 //     arrive as zeros. Each 256 B (d=128) row is stored with its 16 B chunks permuted by an
 //     XOR of the row index, which keeps both the K reads (16 rows, one chunk each) and the
 //     transposed V reads (4 rows, 4 chunks each per 32 lanes) free of bank conflicts.
-//   * Pipeline: K runs two tiles ahead of V. Iteration j issues the loads of K[j+2] and V[j],
+//   * Pipelined kernel (sliding; full on grids of at most one 256-row workgroup per CU):
+//     K runs two tiles ahead of V. Iteration j issues the loads of K[j+2] and V[j],
 //     then computes O += V[j-1] P[j-1] together with the row max of S[j], and the
 //     exponentials of S[j] together with S[j+1] = K[j+1] Q^T; the matrix core and the vector
 //     ALU work on independent data in each half. Two K and two V buffers, one barrier per
@@ -36,11 +38,13 @@
 //     only when a score beats it by more than 2^8 (probabilities stay below 256), so the
 //     accumulator rescale is rare. Row sums are taken over the bf16-rounded probabilities,
 //     the exact weights of the value product: by v_dot2 in the pipelined kernel, by four
-//     small MFMAs per tile in the differential's (whose registers leave room for them).
-//   * The differential runs its own kernel (prefill_diff_kernel, below): each softmax map
-//     gets its own wave (scores on its half of the head dim, values on all of it), and the
-//     two waves of a row block, which share a SIMD, alternate between a matrix phase and a
-//     vector phase one phase apart; they meet once, at the end, through LDS. Its vector
+//     small MFMAs per tile in the phase-separated one (whose registers leave room for them).
+//   * Phase-separated kernel (prefill_phase_kernel, below; the differential, and full on
+//     larger grids): eight waves, two per SIMD, alternate between a matrix phase and a
+//     vector phase one phase apart. For the differential each softmax map gets its own wave
+//     (scores on its half of the head dim, values on all of it) and the two maps of a row
+//     block meet once, at the end, through LDS; for full every wave is a row block of its
+//     own, 256 rows per workgroup, which halves the K/V tile bytes per flop. The vector
 //     phase takes the exponentials against the current reference and leaves the row max to
 //     a rare path at the start of the next matrix phase, taken only while a row has no
 //     reference or when a row's tile sum exceeds 2^8.
@@ -151,7 +155,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(DShape<SPL>::threads,
 prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
                    const __bf16* __restrict__ vg, __bf16* __restrict__ og, int L, int BH,
                    int G, int nq, int window) {
-  static_assert(VAR == kFull || VAR == kSliding, "the differential has its own kernel");
+  static_assert(VAR == kFull || VAR == kSliding, "the differential runs the phase kernel");
   static_assert(SPL == 1 || SPL == 2, "one or two waves per row block");
   constexpr bool kSlide = (VAR == kSliding);
   constexpr int kWaves = DShape<SPL>::waves;
@@ -583,13 +587,18 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   }
 }
 
-// ---------------------------------------------------------------- the differential kernel
+// ---------------------------------------------------------------- the phase-separated kernel
 //
-// Eight waves, two per SIMD: row block rb's two maps are waves rb (map 0) and rb + 4
-// (map 1), and they sit on the same SIMD. Each wave has one map's softmax over half of the
-// head dim and the value product over all of it; the two maps of a row block meet once, at
-// the end, through LDS. The map-1 waves run one phase behind the map-0 waves. Per key tile
-// k a wave runs an M phase (matrix work only: S[k] = K[k] Q^T, then O += V[k-1] P[k-1]) and
+// The differential, and full causal on grids of more than one 256-row workgroup per CU.
+// Eight waves, two per SIMD, in two phase groups: waves w and w + 4 share a SIMD, and the
+// group of waves 4..7 runs one phase behind the group of waves 0..3.
+//   * Differential: row block rb's two maps are waves rb (map 0) and rb + 4 (map 1). Each
+//     wave has one map's softmax over half of the head dim and the value product over all
+//     of it; the two maps of a row block meet once, at the end, through LDS. 128 rows.
+//   * Full: every wave is a row block of its own, scores over the whole head dim. 256 rows,
+//     so each K/V tile brought into LDS serves twice the rows of the pipelined kernel's.
+// Per key tile k a wave runs an M phase (matrix work only: S[k] = K[k] Q^T, then
+// O += V[k-1] P[k-1]) and
 // a V phase (vector work: the exponentials of S[k] into P[k] against the current
 // reference, the loads of later tiles, and four small MFMAs for the row sums of P[k]). The
 // reference test for tile k (no reference yet, or a row's tile sum above 2^8: then the row
@@ -600,25 +609,28 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
 // phases strictly alternate, so one set of score and probability registers is enough.
 // K[k] and V[k-1] (the pair of tile k) live in LDS buffer pair k mod 4; the loads of pair
 // k+3 are issued in the V phase of tile k.
-struct DiffShape {
-  static constexpr int maps = 2;
-  static constexpr int rows = 4;  // 32-row blocks
+template <int VAR>
+struct PhaseShape {
+  static constexpr int maps = VAR == kDifferential ? 2 : 1;
+  static constexpr int rows = 8 / maps;  // 32-row blocks
   static constexpr int waves = rows * maps;
   static constexpr int threads = waves * kWave;
   static constexpr int bm = 32 * rows;
 };
 
-template <int D>
-__global__ void __attribute__((amdgpu_flat_work_group_size(DiffShape::threads,
-                                                           DiffShape::threads),
+template <int D, int VAR>
+__global__ void __attribute__((amdgpu_flat_work_group_size(PhaseShape<VAR>::threads,
+                                                           PhaseShape<VAR>::threads),
                                amdgpu_waves_per_eu(2, 2)))
-prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
-                    const __bf16* __restrict__ vg, __bf16* __restrict__ og, int L, int BH,
-                    int G, int nq, float lambda) {
-  constexpr int kWaves = DiffShape::waves;
-  constexpr int kRows = DiffShape::rows;
-  constexpr int BM = DiffShape::bm;
-  constexpr int NQ = D / 32;  // MFMA steps over one map's d/2 score channels
+prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
+                     const __bf16* __restrict__ vg, __bf16* __restrict__ og, int L, int BH,
+                     int G, int nq, float lambda) {
+  static_assert(VAR == kFull || VAR == kDifferential, "full or differential");
+  constexpr bool kDiff = VAR == kDifferential;
+  constexpr int kWaves = PhaseShape<VAR>::waves;
+  constexpr int kRows = PhaseShape<VAR>::rows;
+  constexpr int BM = PhaseShape<VAR>::bm;
+  constexpr int NQ = kDiff ? D / 32 : D / 16;  // MFMA steps over a map's score channels
   constexpr int DB = D / 32;
   constexpr int ROWB = D * 2;
   constexpr int TILEB = BN * ROWB;
@@ -627,8 +639,8 @@ prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg
   constexpr int CPR = D / 8;
   static_assert(NI % kWaves == 0, "tile loads must split evenly over the waves");
   // LDS: K buffers 0..3, then V buffers 0..3; reused after the key loop to pass map 1's
-  // output to map 0.
-  constexpr int kXchBytes = kRows * 64 * (DB * 16) * 4;
+  // output to map 0 (differential).
+  constexpr int kXchBytes = kDiff ? kRows * 64 * (DB * 16) * 4 : 0;
   constexpr int kSmem = (8 * TILEB > kXchBytes) ? 8 * TILEB : kXchBytes;
   // At the end of an M phase every load but those issued in the wave's last V phase is in.
   constexpr int kWaitOlder = 0x0F70 | (2 * NIW);
@@ -642,7 +654,7 @@ prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int grp = wave_s >> 2;     // phase group (waves w and w + 4 share a SIMD)
   const int rb = wave % kRows;     // row block of this wave
-  const int map = wave / kRows;    // softmax map (differential)
+  const int map = wave / kRows;    // softmax map (differential; 0 for full)
   const int lr = lane & 31;
   const int lg = lane >> 5;
 
@@ -657,7 +669,7 @@ prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg
   const __amdgpu_buffer_rsrc_t Qr = make_rsrc(qg + head, head_bytes);
   const unsigned long long Kbase = reinterpret_cast<unsigned long long>(kg + kv_head);
   const unsigned long long Vbase = reinterpret_cast<unsigned long long>(vg + kv_head);
-  const float c = kLog2e / __builtin_sqrtf((float)(D / 2));
+  const float c = kLog2e / __builtin_sqrtf((float)(kDiff ? D / 2 : D));
   const int ch0 = map * (D / 2);  // first score channel of this wave's map
 
   bf16x8 qf[NQ];
@@ -827,17 +839,19 @@ prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg
           o[db] = mfma32(a, p[kb][h], o[db]);
         }
     // Operand reads ahead of the matrix instructions that use them. A score MFMA reads one
-    // K operand, a value MFMA two V reads: three reads after each score MFMA put the value
-    // product's reads about ten MFMAs ahead when it starts, and one read after each of its
-    // first value MFMAs keeps them ahead to the end of the phase (an even 1.5 reads per
-    // MFMA let the lead fall to one MFMA, less than the LDS latency).
-    constexpr int kLate = 2 * NQ + 8 * DB - 4 - 6 * NQ;  // reads left for the value MFMAs
+    // K operand, a value MFMA two V reads: kEarly reads after each score MFMA (three for the
+    // differential's 8 score MFMAs, two for full's 16) put the value product's reads well
+    // ahead when it starts, and one read after each of its first value MFMAs keeps them
+    // ahead to the end of the phase (an even 1.5 reads per MFMA let the lead fall to one
+    // MFMA, less than the LDS latency).
+    constexpr int kEarly = kDiff ? 3 : 2;
+    constexpr int kLate = 2 * NQ + 8 * DB - 4 - 2 * NQ * kEarly;  // reads for value MFMAs
     static_assert(kLate >= 0 && kLate <= 4 * DB, "read schedule");
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < 2 * NQ; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kEarly, 0);
     }
 #pragma unroll
     for (int i = 0; i < kLate; ++i) {
@@ -897,9 +911,23 @@ prefill_diff_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg
   if (grp == 0) __syncthreads();
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
-  // ---- epilogue: out = O1 / l1 - lambda * O2 / l2, map 1's term passed to map 0 through
-  // LDS. Element (db, r) of a lane is channel db*32 + 8*(r/4) + 4*lg + r%4 of query qi.
+  // ---- epilogue. Element (db, r) of a lane is channel db*32 + 8*(r/4) + 4*lg + r%4 of
+  // query qi.
   const float lsum = l;  // the row-sum MFMAs already add the two lanes of a query
+  if constexpr (!kDiff) {  // out = O / l
+    if (qi < L) {
+      const float inv = 1.0f / lsum;
+      __bf16* orow = og + head + (size_t)qi * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          store4(orow + db * 32 + 8 * r4 + 4 * lg, o[db][r4 * 4] * inv,
+                 o[db][r4 * 4 + 1] * inv, o[db][r4 * 4 + 2] * inv, o[db][r4 * 4 + 3] * inv);
+    }
+    return;
+  }
+  // Differential: out = O1 / l1 - lambda * O2 / l2, map 1's term passed to map 0 through LDS.
   __syncthreads();  // every wave is done reading the tiles
   {
     float* const xch = reinterpret_cast<float*>(smem) + rb * 64 * (DB * 16);
@@ -961,24 +989,42 @@ hipError_t launch_dma_t(const PrefillLaunch& a, hipStream_t stream) {
                     : launch_dma_s<D, VAR, 1>(a, nq, stream);
 }
 
-template <int D>
-hipError_t launch_diff(const PrefillLaunch& a, hipStream_t stream) {
-  constexpr int BM = DiffShape::bm;
-  const int nq = (a.L + BM - 1) / BM;
+template <int D, int VAR>
+hipError_t launch_phase(const PrefillLaunch& a, int nq, hipStream_t stream) {
   const int BH = a.B * a.H;
-  hipLaunchKernelGGL((prefill_diff_kernel<D>), dim3((unsigned)(BH * nq)),
-                     dim3(DiffShape::threads), 0, stream, static_cast<const __bf16*>(a.q),
-                     static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
-                     static_cast<__bf16*>(a.out), a.L, BH, a.H / a.Hkv, nq, a.lambda);
+  hipLaunchKernelGGL((prefill_phase_kernel<D, VAR>), dim3((unsigned)(BH * nq)),
+                     dim3(PhaseShape<VAR>::threads), 0, stream,
+                     static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                     static_cast<const __bf16*>(a.v), static_cast<__bf16*>(a.out), a.L, BH,
+                     a.H / a.Hkv, nq, a.lambda);
   return hipGetLastError();
+}
+
+// Full causal takes the phase-separated kernel (256-row workgroups, one per CU) when its
+// grid is more than one workgroup per CU, so that the later workgroups fill in behind the
+// heavy first ones; on smaller grids the pipelined kernel's two 128-row workgroups per CU
+// (or its key split) balance the causal work better.
+template <int D>
+hipError_t launch_full(const PrefillLaunch& a, hipStream_t stream) {
+  constexpr int BM = PhaseShape<kFull>::bm;
+  const int nq = (a.L + BM - 1) / BM;
+  const long long wgs = (long long)a.B * a.H * nq;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  return wgs > cus ? launch_phase<D, kFull>(a, nq, stream) : launch_dma_t<D, kFull>(a, stream);
 }
 
 template <int D>
 hipError_t launch_dma_v(const PrefillLaunch& a, hipStream_t stream) {
   switch (a.variant) {
-    case kFull: return launch_dma_t<D, kFull>(a, stream);
+    case kFull: return launch_full<D>(a, stream);
     case kSliding: return launch_dma_t<D, kSliding>(a, stream);
-    default: return launch_diff<D>(a, stream);
+    default: {
+      constexpr int BM = PhaseShape<kDifferential>::bm;
+      return launch_phase<D, kDifferential>(a, (a.L + BM - 1) / BM, stream);
+    }
   }
 }
 

@@ -45,13 +45,22 @@ def test_useful_flops_of_the_stack_workload():
 
 
 def test_executed_mfmas_closed_forms():
-    # Full at B=1, H=16, L=8192 (64 query tiles of 128 rows, one wave per row block): query
-    # tile t spans key tiles 0..2t+1, and each of its 4 waves issues 32 MFMAs per tile
-    # (scores 16 + value product 16, the first iteration's value product on zeros standing
-    # in for the one before the first tile); the last tile's value product after the loop
-    # adds 16 for the waves of the last 64 rows, the only ones that see that tile.
-    per_head = sum(4 * 32 * (2 * t + 2) + 2 * 16 for t in range(64))
-    assert bench.executed_mfmas("full", 1, 16, 8192, 128, 0) == 16 * per_head
+    # Full at B=1, H=16, L=4096 on the pipelined kernel (32 query tiles of 128 rows, one
+    # wave per row block; 256 tiles of 256 rows would be one per CU): query tile t spans key
+    # tiles 0..2t+1, and each of its 4 waves issues 32 MFMAs per tile (scores 16 + value
+    # product 16, the first iteration's value product on zeros standing in for the one
+    # before the first tile); the last tile's value product after the loop adds 16 for the
+    # waves of the last 64 rows, the only ones that see that tile.
+    assert not bench.full_takes_phase_kernel(1, 16, 4096)
+    per_head = sum(4 * 32 * (2 * t + 2) + 2 * 16 for t in range(32))
+    assert bench.executed_mfmas("full", 1, 16, 4096, 128, 0) == 16 * per_head
+    # Full at L=8192 on the phase-separated kernel: 32 query tiles of 256 rows, 8 waves,
+    # hi = 4t + 3, hi + 2 matrix phases of 16 + 16 MFMAs, and hi + 2 row-sum passes of 4.
+    assert bench.full_takes_phase_kernel(1, 16, 8192)
+    per_head = sum(8 * (4 * t + 5) * 32 for t in range(32))
+    small = sum(8 * (4 * t + 5) * 4 for t in range(32))
+    assert bench.executed_mfma_split("full", 1, 16, 8192, 128, 0) == (16 * per_head,
+                                                                       16 * small)
     # Differential: 8 waves, hi + 2 matrix phases of 8 + 16 MFMAs each, hi = 2t + 1, and 4
     # row-sum instructions (16x16x32) per exponential pass, hi + 2 passes.
     per_head = sum(8 * (2 * t + 3) * 24 for t in range(64))
@@ -95,7 +104,7 @@ def test_executed_mfmas_match_the_committed_counters():
 def test_write_sq_reads_busy_share_and_clock(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "SQ_FILE", str(tmp_path / "sq_busy.txt"))
     path = tmp_path / "c.csv"
-    name = "_ZN5mixer3dma18prefill_dma_kernelILi128ELi0ELi1EEEvPKDF16b"
+    name = "_ZN5mixer3dma20prefill_phase_kernelILi128ELi0EEEvPKDF16b"
     with open(path, "w") as f:
         f.write('"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value",'
                 '"Start_Timestamp","End_Timestamp"\n')
@@ -133,14 +142,12 @@ def test_write_traffic_scales_by_the_copy_and_reads_back(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "hbm_traffic.txt"))
     mib = 1024  # KiB
     # The copy kernel reads 256 MiB but the fetch counter shows half of it: fetch scale 2.
-    fetch = [("__amd_rocclr_copyBuffer", 128 * mib),
-             ("_ZN5mixer3dma18prefill_dma_kernelILi128ELi0EEEvPKDF16b", 60 * mib),
-             ("_ZN5mixer3dma18prefill_dma_kernelILi128ELi0EEEvPKDF16b", 70 * mib),
-             ("_ZN5mixer3dma19prefill_diff_kernelILi128EEEvPKDF16b", 100 * mib)]
-    write = [("__amd_rocclr_copyBuffer", 256 * mib),
-             ("_ZN5mixer3dma18prefill_dma_kernelILi128ELi0EEEvPKDF16b", 32 * mib),
-             ("_ZN5mixer3dma18prefill_dma_kernelILi128ELi0EEEvPKDF16b", 32 * mib),
-             ("_ZN5mixer3dma19prefill_diff_kernelILi128EEEvPKDF16b", 32 * mib)]
+    full = "_ZN5mixer3dma20prefill_phase_kernelILi128ELi0EEEvPKDF16b"
+    diff = "_ZN5mixer3dma20prefill_phase_kernelILi128ELi2EEEvPKDF16b"
+    fetch = [("__amd_rocclr_copyBuffer", 128 * mib), (full, 60 * mib), (full, 70 * mib),
+             (diff, 100 * mib)]
+    write = [("__amd_rocclr_copyBuffer", 256 * mib), (full, 32 * mib), (full, 32 * mib),
+             (diff, 32 * mib)]
     _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", fetch)
     _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", write)
     bench.write_traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "test")
@@ -153,13 +160,15 @@ def test_write_traffic_scales_by_the_copy_and_reads_back(tmp_path, monkeypatch):
 
 def test_launch_threads_follow_the_launcher():
     # 128-row query tiles; 4 waves per full/sliding workgroup, 8 with the key split (at most
-    # one workgroup per CU) and for the differential. The profiler reported these Grid_Size
+    # one workgroup per CU) and for the differential; full on grids of more than one
+    # 256-row workgroup per CU: 8 waves per 256 rows. The profiler reported these Grid_Size
     # values for the bench's launches.
-    assert bench.launch_threads("full", 1, 16, 8192) == 262144
+    assert bench.launch_threads("full", 1, 16, 8192) == 32 * 16 * 512       # phase kernel
     assert bench.launch_threads("sliding", 1, 16, 8192) == 262144
     assert bench.launch_threads("differential", 1, 16, 8192) == 524288
     assert bench.launch_threads("full", 1, 16, 2048) == 131072       # key split
-    assert bench.launch_threads("full", 1, 16, 32768) == 1048576
+    assert bench.launch_threads("full", 1, 16, 4096) == 512 * 256    # pipelined
+    assert bench.launch_threads("full", 1, 16, 32768) == 128 * 16 * 512
     assert bench.launch_threads("differential", 1, 16, 32768) == 2097152
     assert bench.launch_threads("full", 1, 1, 300) == 3 * 512
 
@@ -169,7 +178,7 @@ def test_counter_summaries_take_the_stack_launches_only(tmp_path, monkeypatch):
     # stay out of the per-launch averages.
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "hbm_traffic.txt"))
     monkeypatch.setattr(bench, "SQ_FILE", str(tmp_path / "sq_busy.txt"))
-    name = "_ZN5mixer3dma18prefill_dma_kernelILi128ELi0ELi1EEEvPKDF16b"
+    name = "_ZN5mixer3dma20prefill_phase_kernelILi128ELi0EEEvPKDF16b"
     stack, other = bench.launch_threads("full", 1, 16, 8192), bench.launch_threads(
         "full", 1, 16, 32768)
     mib = 1024

@@ -279,6 +279,46 @@ def test_key_split_boundary_sampled_rows(torch_cuda, oracle_mod, variant, W, H, 
     assert_close(to_f64(out[:, :, rows]), ref, f"{variant} H={H} L={L} d={d}")
 
 
+# Full causal runs the phase-separated kernel (256-row workgroups) when its grid holds more
+# than one of them per CU (B*H*ceil(L/256) > 256 on MI355X), else the pipelined kernel. Both
+# sides of that boundary at both head dims, against the oracle on sampled rows.
+PHASE_EDGE = [(2, 32768, 128), (2, 32769, 128), (4, 16384, 64), (4, 16385, 64)]
+
+
+@pytest.mark.parametrize("H,L,d", PHASE_EDGE)
+def test_full_phase_kernel_boundary_sampled_rows(torch_cuda, oracle_mod, H, L, d):
+    inp = make(41 + L % 7, 1, H, L, d)
+    out = run_layer(device_tensors(inp), "full", 0, 0.0)
+    rows = sample_rows(L, seed=L, n_random=64, edge=40)
+    ref = _oracle(oracle_mod, inp, "full", 0, 0.0, rows)
+    assert_close(to_f64(out[:, :, rows]), ref, f"full H={H} L={L} d={d}")
+
+
+# The phase-separated full kernel on ragged lengths (not a multiple of its 256 rows or of
+# the 64-key tile), every row against the oracle.
+@pytest.mark.parametrize("B,H,L,d", [(2, 80, 333, 128), (4, 33, 700, 64)])
+def test_full_phase_kernel_every_row(torch_cuda, oracle_mod, B, H, L, d):
+    inp = make(43, B, H, L, d)
+    out = run_layer(device_tensors(inp), "full", 0, 0.0)
+    assert_close(to_f64(out), _oracle(oracle_mod, inp, "full", 0, 0.0),
+                 f"full B={B} H={H} L={L} d={d}")
+
+
+@pytest.mark.parametrize("L", [1, 255, 257, 1000])
+def test_full_phase_kernel_writes_every_row_and_nothing_else(torch_cuda, L):
+    import torch
+    B, H, d = 2, 130, 128  # B*H*ceil(L/256) > 256: the phase-separated kernel
+    inp = make(14, B, H, L, d)
+    q, k, v = device_tensors(inp)
+    n = B * H * L * d
+    buf = torch.full((n + 4096,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    buf[n:] = 1024.0
+    out = buf[:n].view(B, H, L, d)
+    run_layer((q, k, v), "full", 0, 0.0, out=out)
+    assert bool(torch.isfinite(out.float()).all())
+    assert bool((buf[n:].float() == 1024.0).all())
+
+
 @pytest.mark.parametrize("L", [1, 127, 129, 1000])
 @pytest.mark.parametrize("variant", ["full", "sliding", "differential"])
 def test_every_row_written_and_nothing_else(torch_cuda, variant, L):
