@@ -144,11 +144,10 @@ def executed_mfma_split(variant: str, B: int, H: int, L: int, d: int, window: in
             qw = q0 + 32 * rb
             for half in range(spl):
                 j0 = lo + half
-                see_first = (slide and spl == 1) or (
-                    (half == 0 or j0 * bn <= qw + 31) and
-                    (not slide or j0 * bn + bn - 1 >= qw - window + 1))
+                see_first = ((half == 0 or j0 * bn <= qw + 31) and
+                             (not slide or j0 * bn + bn - 1 >= qw - window + 1))
                 jl = lo + spl * (n_it - 1) + half
-                tail = (slide and spl == 1) or jl * bn <= qw + 31
+                tail = jl * bn <= qw + 31
                 total += (qk if see_first else 0) + (n_it - 1) * (qk + pv) + pv + \
                     (pv if tail else 0)
     return B * H * total, 0

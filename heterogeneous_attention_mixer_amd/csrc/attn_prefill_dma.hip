@@ -419,11 +419,8 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   // zeros stand in, and the mask of the first iteration turns every one of them into -inf.
   const int j0_s = lo + half_s;
   const int qw_s = q0 + rb_s * 32;  // the wave's first row, as a scalar
-  // (Not for sliding with SPL = 1, where the branch pushed the kernel past its register
-  // budget.)
-  const bool see_first = (kSlide && SPL == 1) ||
-                         ((half_s == 0 || j0_s * BN <= qw_s + 31) &&
-                          (!kSlide || j0_s * BN + BN - 1 >= qw_s - window + 1));
+  const bool see_first = (half_s == 0 || j0_s * BN <= qw_s + 31) &&
+                         (!kSlide || j0_s * BN + BN - 1 >= qw_s - window + 1);
   float tmax_n;  // row max of the scores of the next tile (unmasked)
   if (see_first) {
     qk_into(std::integral_constant<int, kKBuf[0]>{}, sc[0]);
@@ -528,10 +525,9 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   if (moved_p) scale_o(alpha_p);
   // The last value product, unless no row of this wave sees a key of its last tile (the
   // first rows of a workgroup whose last tile lies past them): its probabilities are all
-  // zero. (Not for sliding with SPL = 1: with the window's extra live values this branch
-  // pushed that kernel past its register budget.)
+  // zero.
   const int jl_s = lo + SPL * it + half_s;
-  if ((kSlide && SPL == 1) || jl_s * BN <= qw_s + 31) {
+  if (jl_s * BN <= qw_s + 31) {
     if (it & 1)
       pv(std::integral_constant<int, kVImm[1]>{}, pr[1]);
     else

@@ -71,8 +71,9 @@ def test_executed_mfmas_closed_forms():
     assert bench.executed_flops("differential", 1, 16, 8192, 128, 0) == 16 * (
         per_head * 32768 + small * 16384)
     # Sliding, W = 1024, a query tile past the first window: 18 key tiles, every wave all of
-    # them (one wave per row block keeps the first scores and the last value product).
-    full_tiles = 4 * (32 * 18 + 16)
+    # them; the waves of rows 64..127 skip the first tile's scores (it lies below their
+    # windows) and those of rows 0..63 the last tile's value product (it lies past them).
+    full_tiles = 4 * (32 * 18 + 16) - 2 * 16 - 2 * 16
     assert bench.executed_mfmas("sliding", 1, 1, 2048, 128, 1024, n_cu=0) - \
         bench.executed_mfmas("sliding", 1, 1, 1920, 128, 1024, n_cu=0) == full_tiles
 
