@@ -46,6 +46,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle SECONDS]
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -115,10 +116,11 @@ def executed_mfma_split(variant: str, B: int, H: int, L: int, d: int, window: in
     Phase-separated kernel, the differential (8 waves: 4 row blocks x 2 maps, 128 rows) and
     full causal on grids of more than one 256-row workgroup per CU (8 waves: 8 row blocks):
     per wave hi + 2 matrix phases of the scores (half-width for the differential) and the
-    value product each, and four 16x16x32 row-sum instructions per exponential pass: one
-    per vector phase (hi + 1) and one more for the first tile, which is taken again once
-    its rows have a reference. Passes taken again because a tile's sum exceeds 2^8 depend
-    on the data and are not counted (none on the bench's inputs)."""
+    value product each (the first value product multiplies zeros, the last scores are
+    discarded), and four 16x16x32 row-sum instructions per exponential pass: one
+    per vector phase after the first (hi), and one for the first tile, taken once its rows
+    have a reference (its own vector phase takes none). Passes taken again because a tile's
+    sum exceeds 2^8 depend on the data and are not counted (none on the bench's inputs)."""
     bm, bn = 128, 64
     nq = (L + bm - 1) // bm
     qk = 2 * (d // 16)          # one tile's scores: 2 key blocks x d/16 steps
@@ -132,7 +134,7 @@ def executed_mfma_split(variant: str, B: int, H: int, L: int, d: int, window: in
         for qt in range((L + rows - 1) // rows):
             hi = (min(qt * rows + rows, L) - 1) // bn
             total += 8 * (hi + 2) * (qk_phase + pv)
-            small += 8 * (hi + 2) * 4
+            small += 8 * (hi + 1) * 4
         return B * H * total, B * H * small
     spl = 2 if B * H * nq <= n_cu else 1
     for qt in range(nq):
@@ -454,6 +456,9 @@ def main(argv=None) -> int:
               "would shard over batch and heads with no exchange, which is not implemented)",
               file=sys.stderr)
         return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: --steps must be at least 1 and --warmup at least 0", file=sys.stderr)
+        return 2
 
     import torch
 
@@ -531,13 +536,21 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    start.record()
-    for i in range(K):
-        step(layer_events[i])
-    end.record()
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
+    # A full collection of Python's cyclic garbage takes milliseconds in a process that has
+    # torch loaded, and the argument arrays each step builds can trigger one: collect now and
+    # hold the collector off until the device has finished.
+    gc.collect()
+    gc.disable()
+    try:
+        t_wall = time.perf_counter()
+        start.record()
+        for i in range(K):
+            step(layer_events[i])
+        end.record()
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter() - t_wall
+    finally:
+        gc.enable()
     ms_per_step = start.elapsed_time(end) / K
 
     total_flops = sum(useful_flops(VARIANT_NAMES[v], B, H, L, d, W) for v in sched)
@@ -548,6 +561,15 @@ def main(argv=None) -> int:
         for layer in range(n_layers):
             per_launch[VARIANT_NAMES[sched[layer]]].append(
                 evs[layer].elapsed_time(evs[layer + 1]))
+    # Device time in the timed region outside every layer's events: before the first layer,
+    # between steps and after the last. Near zero when the host keeps the queue full; a
+    # large figure means the device waited on the host (the value still counts it).
+    gaps = ([start.elapsed_time(layer_events[0][0])]
+            + [layer_events[i][n_layers].elapsed_time(layer_events[i + 1][0])
+               for i in range(K - 1)]
+            + [layer_events[-1][n_layers].elapsed_time(end)])
+    outside_layers = {"ms_total": round(sum(gaps), 5), "ms_max": round(max(gaps), 5),
+                      "max_before_step": gaps.index(max(gaps))}
     per_variant = {}
     for name, ts in per_launch.items():
         if not ts:
@@ -774,6 +796,7 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "wall_s_timed": round(t_wall, 4),
+        "timed_outside_layers": outside_layers,
     }
     line["memory"] = memory
     line["arms"] = arms or None

@@ -705,9 +705,14 @@ prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ k
   auto load_tile = [&](bool v, int dst, int j) {
     const u32x4 r = rsrc_words((v ? Vbase : Kbase) + (unsigned long long)j * TILEB,
                                head_bytes - j * TILEB);
+    // The LDS destination is formed here, behind an empty statement: left visible, the
+    // compiler keeps every buffer pair's destinations live across the unrolled key loop and
+    // runs out of scalar registers.
+    unsigned m0b = lds_addr + (unsigned)wave_s * 1024u + (unsigned)dst;
+    asm volatile("" : "+s"(m0b));
 #pragma unroll
     for (int t = 0; t < NIW; ++t)
-      lds_load16(r, (unsigned)(lds_addr + dst + (wave_s + t * kWaves) * 1024), ld_off[t]);
+      lds_load16(r, m0b + (unsigned)(t * kWaves * 1024), ld_off[t]);
   };
   // Does every row of the wave see every key of tile j?
   auto full_tile = [&](int j) { return j * BN + BN - 1 <= qw; };
@@ -795,9 +800,11 @@ prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ k
     }
     l += lt;
   };
-  // M phase of tile k (pair buffer `pb`): S = K[k] Q^T; O += V[k-1] P.
-  auto m_phase = [&](int pb) {
-    const int kbase = pb * TILEB;
+  // M phase of tile k (pair buffer `pb`, a compile-time constant, so that every operand
+  // read's LDS offset is an instruction immediate): S = K[k] Q^T; O += V[k-1] P.
+  auto m_phase = [&](auto pb_c) {
+    constexpr int pb = decltype(pb_c)::value;
+    constexpr int kbase = pb * TILEB;
     int ka[NQ], va[DB][2];
 #pragma unroll
     for (int kk = 0; kk < NQ; ++kk) ka[kk] = k_off[kk] + kbase;
@@ -872,7 +879,9 @@ prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ k
         for (int r = 0; r < 16; ++r)
           if (kb * 32 + 8 * (r >> 2) + (r & 3) > t) s[kb][r] = -INFINITY;
     }
-    take_exps();
+    // The first tile's rows have no reference yet, so the next M phase's test always takes
+    // its rare path, which takes the exponentials and sums again: none here.
+    if (k > lo) take_exps();
   };
 
   // ---- prologue (lo is tile 0): pair 0 = (K[0], zeros), pair 1 = (K[1], V[0]),
@@ -894,16 +903,35 @@ prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ k
   // ---- key loop: group 1 runs one phase behind group 0; both run the same number of
   // barriers. The last M phase (tile hi+1) only adds V[hi] P[hi]; its scores are discarded.
   if (grp == 1) __syncthreads();
-  for (int k = lo; k <= hi + 1; ++k) {
+  // The loop is unrolled by the four buffer pairs (tile k uses pair k mod 4; lo is 0 here).
+  auto step = [&](auto pb_c, int k) {
     if (k > lo) settle();  // tile k-1
     __builtin_amdgcn_s_setprio(1);
-    m_phase((k - lo) & 3);
+    m_phase(pb_c);
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(kWaitOlder);
     __syncthreads();
     if (k <= hi) v_phase(k);
     __syncthreads();
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
+  int k = lo;
+  for (; k + 3 <= hi + 1; k += 4) {
+    step(P0{}, k);
+    step(P1{}, k + 1);
+    step(P2{}, k + 2);
+    step(P3{}, k + 3);
   }
+  if (k <= hi + 1) step(P0{}, k++);
+  if (k <= hi + 1) step(P1{}, k++);
+  if (k <= hi + 1) step(P2{}, k++);
+  // The last M phase's scores are discarded; reading them here keeps the compiler from
+  // dropping them only where it can prove which step comes last (every workgroup then
+  // issues the same matrix work for its tile range).
+  asm volatile("" ::"v"(s[0]), "v"(s[1]));
   if (grp == 0) __syncthreads();
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
 

@@ -55,16 +55,16 @@ def test_executed_mfmas_closed_forms():
     per_head = sum(4 * 32 * (2 * t + 2) + 2 * 16 for t in range(32))
     assert bench.executed_mfmas("full", 1, 16, 4096, 128, 0) == 16 * per_head
     # Full at L=8192 on the phase-separated kernel: 32 query tiles of 256 rows, 8 waves,
-    # hi = 4t + 3, hi + 2 matrix phases of 16 + 16 MFMAs, and hi + 2 row-sum passes of 4.
+    # hi = 4t + 3, hi + 2 matrix phases of 16 + 16 MFMAs, and hi + 1 row-sum passes of 4.
     assert bench.full_takes_phase_kernel(1, 16, 8192)
     per_head = sum(8 * (4 * t + 5) * 32 for t in range(32))
-    small = sum(8 * (4 * t + 5) * 4 for t in range(32))
+    small = sum(8 * (4 * t + 4) * 4 for t in range(32))
     assert bench.executed_mfma_split("full", 1, 16, 8192, 128, 0) == (16 * per_head,
                                                                        16 * small)
     # Differential: 8 waves, hi + 2 matrix phases of 8 + 16 MFMAs each, hi = 2t + 1, and 4
-    # row-sum instructions (16x16x32) per exponential pass, hi + 2 passes.
+    # row-sum instructions (16x16x32) per exponential pass, hi + 1 passes.
     per_head = sum(8 * (2 * t + 3) * 24 for t in range(64))
-    small = sum(8 * (2 * t + 3) * 4 for t in range(64))
+    small = sum(8 * (2 * t + 2) * 4 for t in range(64))
     assert bench.executed_mfma_split("differential", 1, 16, 8192, 128, 0) == (
         16 * per_head, 16 * small)
     assert bench.executed_mfmas("differential", 1, 16, 8192, 128, 0) == 16 * (per_head + small)
