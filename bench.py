@@ -170,23 +170,26 @@ def executed_flops(variant: str, B: int, H: int, L: int, d: int, window: int,
 
 
 def launch_threads(variant: str, B: int, H: int, L: int, n_cu: int = N_CU) -> int:
-    """Work-items in one launch of the d=128 bf16 kernel (the Grid_Size profilers report):
-    one workgroup per (b*h, 128-row query tile); 256 work-items per full/sliding workgroup,
-    512 with the key split (grids of at most one workgroup per CU) and for the
-    differential; full on the phase-separated kernel, one 512-item workgroup per 256-row
-    query tile."""
-    if variant == "full" and full_takes_phase_kernel(B, H, L, n_cu):
-        return B * H * ((L + 255) // 256) * 512
+    """Work-items in one launch of the d=128 bf16 kernel (the Grid_Size profilers report).
+    Full and sliding on the pipelined kernel: one workgroup per (b*h, 128-row query tile), of
+    256 work-items, 512 with the key split (grids of at most one workgroup per CU). The
+    phase-separated kernel (the differential with 128-row units, full causal with 256-row
+    units on grids of more than one of them per CU): 512-item workgroups, one per unit, or,
+    with more units than CUs, the persistent launch of one per CU."""
+    if variant == "differential" or (variant == "full" and
+                                     full_takes_phase_kernel(B, H, L, n_cu)):
+        rows = 128 if variant == "differential" else 256
+        return min(B * H * ((L + rows - 1) // rows), n_cu) * 512
     wgs = B * H * ((L + 127) // 128)
-    if variant == "differential" or wgs <= n_cu:
-        return wgs * 512
-    return wgs * 256
+    return wgs * 512 if wgs <= n_cu else wgs * 256
 
 
 def _stack_dispatch(variant: str, row: dict) -> bool:
-    """Whether a profiler row belongs to a launch of the stack workload (B=1 H=16 L=8192):
-    the counter summaries average those only, not the other lengths the same run times. Rows
-    without a Grid_Size column are taken as they are."""
+    """Whether a profiler row can belong to a launch of the stack workload (B=1 H=16
+    L=8192), by its grid. The persistent launches of the phase-separated kernel have one
+    workgroup per CU at every length, so the counter runs time the stack alone
+    (--no-sweep --no-gqa --no-extras); this keeps out the launches a grid does tell apart.
+    Rows without a Grid_Size column are taken as they are."""
     g = row.get("Grid_Size")
     if not g:
         return True

@@ -53,7 +53,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
+#include <utility>
+#include <vector>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -605,6 +608,36 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
 // phases strictly alternate, so one set of score and probability registers is enough.
 // K[k] and V[k-1] (the pair of tile k) live in LDS buffer pair k mod 4; the loads of pair
 // k+3 are issued in the V phase of tile k.
+// Work queues of the persistent launch. A slot holds one counter per XCD queue (each on a
+// 64-byte line of its own) and a count of the workgroups that have finished; the last
+// workgroup to finish sets them all back to zero, so a slot is clean between launches. The
+// host gives each stream a slot of its own: launches on one stream run one after another,
+// and launches that may overlap never share a slot.
+constexpr int kQueueSlots = 256;
+constexpr int kQueues = 8;
+constexpr int kSlotWords = (kQueues + 1) * 16;
+__device__ unsigned g_unit_queue[kQueueSlots * kSlotWords];
+
+// What the phase kernel keeps in LDS between units.
+struct UnitArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  __bf16* o;
+  float lambda;
+  int BH, G, nq, slot, grid;
+  int ux, ut;  // queue and ticket of the current unit (ux < 0: no more units)
+};
+// A wave-uniform value read from LDS, as a scalar.
+__device__ __forceinline__ int rfl(int x) { return __builtin_amdgcn_readfirstlane(x); }
+template <typename T>
+__device__ __forceinline__ T* rfl_ptr(T* p) {
+  const unsigned long long u = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)u);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(u >> 32));
+  return reinterpret_cast<T*>(((unsigned long long)hi << 32) | lo);
+}
+
 template <int VAR>
 struct PhaseShape {
   static constexpr int maps = VAR == kDifferential ? 2 : 1;
@@ -620,7 +653,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(PhaseShape<VAR>::thre
                                amdgpu_waves_per_eu(2, 2)))
 prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
                      const __bf16* __restrict__ vg, __bf16* __restrict__ og, int L, int BH,
-                     int G, int nq, float lambda) {
+                     int G, int nq, float lambda, int slot) {
   static_assert(VAR == kFull || VAR == kDifferential, "full or differential");
   constexpr bool kDiff = VAR == kDifferential;
   constexpr int kWaves = PhaseShape<VAR>::waves;
@@ -653,25 +686,9 @@ prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ k
   const int map = wave / kRows;    // softmax map (differential; 0 for full)
   const int lr = lane & 31;
   const int lg = lane >> 5;
-
-  int bh, qt;
-  map_unit(blockIdx.x, BH, nq, &bh, &qt);
-  const int q0 = qt * BM;
-  const int qw = q0 + rb * 32;
-  const int qi = qw + lr;
-  const size_t head = (size_t)bh * (size_t)L * D;
-  const size_t kv_head = (size_t)(bh / G) * (size_t)L * D;
-  const int head_bytes = L * ROWB;
-  const __amdgpu_buffer_rsrc_t Qr = make_rsrc(qg + head, head_bytes);
-  const unsigned long long Kbase = reinterpret_cast<unsigned long long>(kg + kv_head);
-  const unsigned long long Vbase = reinterpret_cast<unsigned long long>(vg + kv_head);
   const float c = kLog2e / __builtin_sqrtf((float)(kDiff ? D / 2 : D));
   const int ch0 = map * (D / 2);  // first score channel of this wave's map
-
-  bf16x8 qf[NQ];
-#pragma unroll
-  for (int kk = 0; kk < NQ; ++kk) qf[kk] = bload8<__bf16>(Qr, qi * D + ch0 + kk * 16 + lg * 8);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  const int head_bytes = L * ROWB;
 
   // Per-lane address parts (the same chunk swizzle and read patterns as the pipelined
   // kernel; V offsets carry the V region's base).
@@ -697,6 +714,58 @@ prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ k
       const int chunk = 4 * db + 2 * vdh + ((vs & 3) >> 1);
       v_off[db][rr] = 4 * TILEB + r * ROWB + ((chunk ^ swz<D>(r)) << 4) + (vs & 1) * 8;
     }
+  // Row sums on the matrix core: v_mfma_f32_16x16x32_bf16 with a 0/1 selector as A and a
+  // probability register as B. As B, lane l's register is k-group l/16 of column l%16; it
+  // holds 8 probabilities of query l%32, so query n (< 16) fills k-groups 0 and 2 of column
+  // n and query n+16 k-groups 1 and 3. Selector rows 0 and 8 take k-groups 0 and 2, rows 4
+  // and 12 take 1 and 3, and the result's element 0 in lane l is row 4*(l/16) of column
+  // l%16: the whole row sum of query l%32, in both lanes of the query. Four of these
+  // (16 cycles each on the matrix pipe) replace 16 v_dot2c, each of which holds the matrix
+  // pipe for about 10 cycles, out of the vector phase that runs beside the partner's MFMAs.
+  bf16x8 rsel;
+  {
+    const int sr = lane & 15, sg = (lane >> 4) & 1;
+    const bool one = ((sr == 0 || sr == 8) && sg == 0) || ((sr == 4 || sr == 12) && sg == 1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rsel[e] = one ? (__bf16)1.0f : (__bf16)0.0f;
+  }
+
+  // Units: (head, query tile) pairs. With the head count a multiple of 8 there is one queue
+  // per XCD, holding that XCD's heads heaviest tile first (the order map_unit deals them);
+  // otherwise one queue. Workgroup b starts on ticket b / nQ of queue b % nQ (its XCD's, as
+  // the hardware deals workgroups to the XCDs round-robin). With a slot (the persistent
+  // launch, one workgroup per CU), it then takes the next ticket of that queue, and once
+  // that queue is empty, tickets of the others; without one (one workgroup per unit) it
+  // stops after its first unit.
+  // The launch's arguments and the current unit live in LDS between units, read back where
+  // they are used: kept in scalar registers across the key loop they would not fit.
+  __shared__ UnitArgs ua;
+  if (tid == 0) {
+    const int nQ = ((BH & 7) == 0) ? kQueues : 1;
+    ua = UnitArgs{qg, kg, vg, og, lambda, BH, G, nq, slot, (int)gridDim.x,
+                  (int)blockIdx.x % nQ, (int)blockIdx.x / nQ};
+  }
+  __syncthreads();
+  for (;;) {
+  int bh, qt;
+  {
+    const int BHu = rfl(ua.BH), nqu = rfl(ua.nq);
+    const int nQ = ((BHu & 7) == 0) ? kQueues : 1;
+    map_unit(rfl(ua.ut) * nQ + rfl(ua.ux), BHu, nqu, &bh, &qt);
+  }
+  const int q0 = qt * BM;
+  const int qw = q0 + rb * 32;
+  const int qi = qw + lr;
+  const size_t head = (size_t)bh * (size_t)L * D;
+  const size_t kv_head = (size_t)(bh / rfl(ua.G)) * (size_t)L * D;
+  const __amdgpu_buffer_rsrc_t Qr = make_rsrc(rfl_ptr(ua.q) + head, head_bytes);
+  const unsigned long long Kbase = reinterpret_cast<unsigned long long>(rfl_ptr(ua.k) + kv_head);
+  const unsigned long long Vbase = reinterpret_cast<unsigned long long>(rfl_ptr(ua.v) + kv_head);
+
+  bf16x8 qf[NQ];
+#pragma unroll
+  for (int kk = 0; kk < NQ; ++kk) qf[kk] = bload8<__bf16>(Qr, qi * D + ch0 + kk * 16 + lg * 8);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
   const int q_last = min(q0 + BM, L) - 1;
   const int lo = 0;
@@ -724,21 +793,6 @@ prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ k
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   float m = -INFINITY, l = 0.0f;
   float lt = 0.0f;  // the row's sum of the last tile's probabilities, not yet in l
-  // Row sums on the matrix core: v_mfma_f32_16x16x32_bf16 with a 0/1 selector as A and a
-  // probability register as B. As B, lane l's register is k-group l/16 of column l%16; it
-  // holds 8 probabilities of query l%32, so query n (< 16) fills k-groups 0 and 2 of column
-  // n and query n+16 k-groups 1 and 3. Selector rows 0 and 8 take k-groups 0 and 2, rows 4
-  // and 12 take 1 and 3, and the result's element 0 in lane l is row 4*(l/16) of column
-  // l%16: the whole row sum of query l%32, in both lanes of the query. Four of these
-  // (16 cycles each on the matrix pipe) replace 16 v_dot2c, each of which holds the matrix
-  // pipe for about 10 cycles, out of the vector phase that runs beside the partner's MFMAs.
-  bf16x8 rsel;
-  {
-    const int sr = lane & 15, sg = (lane >> 4) & 1;
-    const bool one = ((sr == 0 || sr == 8) && sg == 0) || ((sr == 4 || sr == 12) && sg == 1);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) rsel[e] = one ? (__bf16)1.0f : (__bf16)0.0f;
-  }
   floatx16 s[2];
   bf16x8 p[2][2];
 #pragma unroll
@@ -932,8 +986,29 @@ prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ k
   // dropping them only where it can prove which step comes last (every workgroup then
   // issues the same matrix work for its tile range).
   asm volatile("" ::"v"(s[0]), "v"(s[1]));
-  if (grp == 0) __syncthreads();
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  // Group 0 ends its key loop one phase before group 1. Once its own tile loads are in, wave
+  // 0 asks for the next unit, so that the answer comes back while the workgroup finishes:
+  // lane 0 takes the next ticket of the current queue, and lanes 32.. read every queue's
+  // counter in the same round trip, for when the current queue turns out empty. With no
+  // tile load of the wave in flight, the key loop's counted waits are not disturbed.
+  unsigned tk_next = 0;
+  unsigned q_seen = 0;
+  if (grp == 0) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    if (wave_s == 0 && ua.slot >= 0) {
+      unsigned* const qs = g_unit_queue + ua.slot * kSlotWords;
+      const int nQ = ((ua.BH & 7) == 0) ? kQueues : 1;
+      if (lane == 0)
+        tk_next = __hip_atomic_fetch_add(qs + 16 * ua.ux, 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+      else if (lane >= 32 && lane < 32 + nQ)
+        q_seen = __hip_atomic_load(qs + 16 * (lane - 32), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+  } else {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  }
 
   // ---- epilogue. Element (db, r) of a lane is channel db*32 + 8*(r/4) + 4*lg + r%4 of
   // query qi.
@@ -941,7 +1016,7 @@ prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ k
   if constexpr (!kDiff) {  // out = O / l
     if (qi < L) {
       const float inv = 1.0f / lsum;
-      __bf16* orow = og + head + (size_t)qi * D;
+      __bf16* orow = rfl_ptr(ua.o) + head + (size_t)qi * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -949,14 +1024,13 @@ prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ k
           store4(orow + db * 32 + 8 * r4 + 4 * lg, o[db][r4 * 4] * inv,
                  o[db][r4 * 4 + 1] * inv, o[db][r4 * 4 + 2] * inv, o[db][r4 * 4 + 3] * inv);
     }
-    return;
-  }
+  } else {
   // Differential: out = O1 / l1 - lambda * O2 / l2, map 1's term passed to map 0 through LDS.
   __syncthreads();  // every wave is done reading the tiles
   {
     float* const xch = reinterpret_cast<float*>(smem) + rb * 64 * (DB * 16);
     if (map == 1) {
-      const float sc = lambda / lsum;
+      const float sc = ua.lambda / lsum;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -964,11 +1038,10 @@ prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ k
     }
   }
   __syncthreads();
-  if (map == 1) return;
-  if (qi < L) {
+  if (map == 0 && qi < L) {
     const float inv = 1.0f / lsum;
     const float* const xch = reinterpret_cast<const float*>(smem) + rb * 64 * (DB * 16);
-    __bf16* orow = og + head + (size_t)qi * D;
+    __bf16* orow = rfl_ptr(ua.o) + head + (size_t)qi * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -981,6 +1054,65 @@ prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ k
         }
         store4(orow + db * 32 + 8 * r4 + 4 * lg, x[0], x[1], x[2], x[3]);
       }
+  }
+  }
+
+  if (rfl(ua.slot) < 0) break;
+  // Wave 0 settles the next unit. When the current queue is empty it takes a ticket from the
+  // queue with the most left, by the counters read with the request (lanes 32..) and read
+  // again after every miss; a queue found empty stays empty, so this ends after at most nQ
+  // misses.
+  if (wave_s == 0) {
+    const int nQ = ((rfl(ua.BH) & 7) == 0) ? kQueues : 1;
+    const int Ux = rfl(ua.BH) * rfl(ua.nq) / nQ;
+    unsigned* const qslot = g_unit_queue + rfl(ua.slot) * kSlotWords;
+    // Tickets below this were dealt to the workgroups as their first units.
+    auto first_dyn = [&](int x) { return (rfl(ua.grid) - x + nQ - 1) / nQ; };
+    const int ux = rfl(ua.ux);
+    int nx = ux;
+    int nt = first_dyn(ux) + __builtin_amdgcn_readfirstlane((int)tk_next);
+    bool reread = false;
+    while (nt >= Ux) {
+      if (reread && lane >= 32 && lane < 32 + nQ)
+        q_seen = __hip_atomic_load(qslot + 16 * (lane - 32), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+      reread = true;
+      nx = -1;
+      int most = 0;
+      for (int x = 0; x < nQ; ++x) {
+        const int v = Ux - first_dyn(x) - (int)__builtin_amdgcn_readlane(q_seen, 32 + x);
+        if (v > most) {
+          most = v;
+          nx = x;
+        }
+      }
+      if (nx < 0) break;
+      unsigned t = 0;
+      if (lane == 0)
+        t = __hip_atomic_fetch_add(qslot + 16 * nx, 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+      nt = first_dyn(nx) + __builtin_amdgcn_readfirstlane((int)t);
+    }
+    if (lane == 0) {
+      ua.ux = nx;
+      ua.ut = nt;
+    }
+  }
+  __syncthreads();
+  if (rfl(ua.ux) < 0) break;
+  }  // units
+
+  // The last workgroup to finish returns the slot's counters to zero for the next launch.
+  // The counters are only ever touched by device-scope atomics, and every workgroup's ticket
+  // requests have returned before it counts itself here, so no ordering beyond that of the
+  // atomics themselves is needed (and none that would flush the L2).
+  if (tid == 0 && ua.slot >= 0) {
+    unsigned* const qslot = g_unit_queue + ua.slot * kSlotWords;
+    if (__hip_atomic_fetch_add(qslot + 16 * kQueues, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT) == (unsigned)ua.grid - 1) {
+      for (int x = 0; x <= kQueues; ++x)
+        __hip_atomic_store(qslot + 16 * x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -1013,14 +1145,42 @@ hipError_t launch_dma_t(const PrefillLaunch& a, hipStream_t stream) {
                     : launch_dma_s<D, VAR, 1>(a, nq, stream);
 }
 
+// The queue slot of (device, stream): the stream's rank among the streams of that device
+// that have launched the persistent kernel, or -1 once every slot has an owner. Launches on
+// one stream run in order, so they share its slot safely; a slot never passes to another
+// stream. A graph captured from a stream keeps that stream's slot.
+int queue_slot(int dev, hipStream_t stream) {
+  static std::mutex mu;
+  static std::vector<std::pair<int, hipStream_t>> owners;
+  std::lock_guard<std::mutex> hold(mu);
+  int n = 0;
+  for (const auto& o : owners) {
+    if (o.first != dev) continue;
+    if (o.second == stream) return n;
+    ++n;
+  }
+  if (n >= kQueueSlots) return -1;
+  owners.emplace_back(dev, stream);
+  return n;
+}
+
 template <int D, int VAR>
 hipError_t launch_phase(const PrefillLaunch& a, int nq, hipStream_t stream) {
   const int BH = a.B * a.H;
-  hipLaunchKernelGGL((prefill_phase_kernel<D, VAR>), dim3((unsigned)(BH * nq)),
-                     dim3(PhaseShape<VAR>::threads), 0, stream,
-                     static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+  const long long units = (long long)BH * nq;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  // One workgroup holds a CU (its LDS). With more units than CUs the launch is persistent:
+  // one workgroup per CU, taking units from the stream's queue slot; otherwise (or with
+  // every slot taken) one workgroup per unit.
+  const int slot = units > cus ? queue_slot(dev, stream) : -1;
+  const unsigned grid = slot >= 0 ? (unsigned)cus : (unsigned)units;
+  hipLaunchKernelGGL((prefill_phase_kernel<D, VAR>), dim3(grid), dim3(PhaseShape<VAR>::threads),
+                     0, stream, static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                      static_cast<const __bf16*>(a.v), static_cast<__bf16*>(a.out), a.L, BH,
-                     a.H / a.Hkv, nq, a.lambda);
+                     a.H / a.Hkv, nq, a.lambda, slot);
   return hipGetLastError();
 }
 

@@ -12,7 +12,15 @@
  *     shape; H counts query heads and key/value heads alike (multi-head attention), except
  *     in mixer_prefill_gqa_async, whose k and v have Hkv heads.
  *   - Ownership: the caller allocates and owns every buffer. The library allocates no device
- *     memory, keeps no state between calls and never synchronises the device.
+ *     memory and never synchronises the device. Its only state is a set of work-queue
+ *     counters for the persistent launch of full causal (on grids of more 256-row query
+ *     tiles than CUs) and of the differential: 256 slots per device in the library's own
+ *     device memory (set up, zeroed, when the library is loaded), one slot per stream that
+ *     makes such a launch, back at zero when each launch ends. Launches on one stream share
+ *     its slot; launches on different streams never share one. A HIP graph captured from a
+ *     stream keeps that stream's slot: a replay must not run while another launch made on
+ *     that stream, or another replay of the graph, may be running. A stream that finds
+ *     every slot taken gets the one-workgroup-per-tile launch, with the same results.
  *   - Asynchrony: the *_async calls and mixer_stack_prefill enqueue work on `stream` (a
  *     hipStream_t passed as void*, NULL = the legacy default stream) and return. Launch
  *     errors come back as MIXER_EHIP; a fault during execution surfaces at the caller's next

@@ -160,18 +160,22 @@ def test_write_traffic_scales_by_the_copy_and_reads_back(tmp_path, monkeypatch):
 
 
 def test_launch_threads_follow_the_launcher():
-    # 128-row query tiles; 4 waves per full/sliding workgroup, 8 with the key split (at most
-    # one workgroup per CU) and for the differential; full on grids of more than one
-    # 256-row workgroup per CU: 8 waves per 256 rows. The profiler reported these Grid_Size
-    # values for the bench's launches.
-    assert bench.launch_threads("full", 1, 16, 8192) == 32 * 16 * 512       # phase kernel
+    # Pipelined kernel: 128-row query tiles, 4 waves per full/sliding workgroup, 8 with the
+    # key split (at most one workgroup per CU). Phase-separated kernel (the differential's
+    # 128-row units; full's 256-row units on grids of more of them than CUs): 8 waves per
+    # unit, or one workgroup per CU (persistent) when there are more units than CUs. The
+    # profiler reported these Grid_Size values for the bench's launches.
+    assert bench.launch_threads("full", 1, 16, 8192) == 256 * 512         # persistent
     assert bench.launch_threads("sliding", 1, 16, 8192) == 262144
-    assert bench.launch_threads("differential", 1, 16, 8192) == 524288
+    assert bench.launch_threads("differential", 1, 16, 8192) == 256 * 512  # persistent
     assert bench.launch_threads("full", 1, 16, 2048) == 131072       # key split
     assert bench.launch_threads("full", 1, 16, 4096) == 512 * 256    # pipelined
-    assert bench.launch_threads("full", 1, 16, 32768) == 128 * 16 * 512
-    assert bench.launch_threads("differential", 1, 16, 32768) == 2097152
+    assert bench.launch_threads("full", 1, 16, 32768) == 256 * 512
+    assert bench.launch_threads("differential", 1, 16, 32768) == 256 * 512
+    assert bench.launch_threads("differential", 1, 16, 2048) == 256 * 512  # one per unit
+    assert bench.launch_threads("differential", 1, 2, 2048) == 32 * 512
     assert bench.launch_threads("full", 1, 1, 300) == 3 * 512
+    assert bench.launch_threads("full", 2, 80, 333) == 256 * 512
 
 
 def test_counter_summaries_take_the_stack_launches_only(tmp_path, monkeypatch):
@@ -179,9 +183,9 @@ def test_counter_summaries_take_the_stack_launches_only(tmp_path, monkeypatch):
     # stay out of the per-launch averages.
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "hbm_traffic.txt"))
     monkeypatch.setattr(bench, "SQ_FILE", str(tmp_path / "sq_busy.txt"))
-    name = "_ZN5mixer3dma20prefill_phase_kernelILi128ELi0EEEvPKDF16b"
-    stack, other = bench.launch_threads("full", 1, 16, 8192), bench.launch_threads(
-        "full", 1, 16, 32768)
+    name = "_ZN5mixer3dma17prefill_dma_kernelILi128ELi1ELi1EEEvPKDF16b"
+    stack, other = bench.launch_threads("sliding", 1, 16, 8192), bench.launch_threads(
+        "sliding", 1, 16, 32768)
     mib = 1024
     for counter, copy_kib, kib in (("FETCH_SIZE", 256 * mib, (10 * mib, 999 * mib)),
                                    ("WRITE_SIZE", 256 * mib, (4 * mib, 99 * mib))):
@@ -192,7 +196,7 @@ def test_counter_summaries_take_the_stack_launches_only(tmp_path, monkeypatch):
             f.write(f'3,{other},"{name}","{counter}",{kib[1]}\n')
     bench.write_traffic(str(tmp_path / "FETCH_SIZE.csv"), str(tmp_path / "WRITE_SIZE.csv"),
                         "test")
-    assert bench.read_traffic("full") == pytest.approx(14 * 1024 * 1024)
+    assert bench.read_traffic("sliding") == pytest.approx(14 * 1024 * 1024)
     with open(tmp_path / "sq.csv", "w") as f:
         f.write('"Dispatch_Id","Grid_Size","Kernel_Name","Counter_Name","Counter_Value",'
                 '"Start_Timestamp","End_Timestamp"\n')
@@ -201,7 +205,7 @@ def test_counter_summaries_take_the_stack_launches_only(tmp_path, monkeypatch):
                            ("GRBM_GUI_ACTIVE", 8 * 1000)):
                 f.write(f'{did},{grid},"{name}","{cn}",{cv},1000,1500\n')
     bench.write_sq(str(tmp_path / "sq.csv"), "test")
-    sq = bench.read_sq("full")
+    sq = bench.read_sq("sliding")
     assert sq["mfma_busy"] == pytest.approx(0.5) and sq["sq_insts_mfma"] == 1
 
 
