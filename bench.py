@@ -12,6 +12,7 @@ resident in HBM. The nine launches go back to back on one stream through
 Reported (one JSON line):
   value           useful attention TFLOP/s of the whole step (4*d flops per visible
                   query-key pair, summed over the nine layers, / step time);
+  per_position    each of the nine layers' median time, in schedule order;
   per_variant     per-layer kernel time and useful TFLOP/s of each variant at L=8K, from HIP
                   events recorded between the launches inside the timed steps, and the
                   fraction of the dense bf16 MFMA peak; the executed rate counts the matrix
@@ -21,8 +22,9 @@ Reported (one JSON line):
                   the kernel source;
   roofline        the same for the kernel that takes most of the step time, with its HBM
                   traffic and matrix-pipe busy share from the committed counter summaries;
-  sweep           the other lengths of Table 3 (sec. 4.2): full at L=2K and 32K, the
-                  differential at 32K (on by default; --no-sweep skips it);
+  sweep           the lengths of Table 3 (sec. 4.2) for one layer type at a time, launched
+                  back to back: full at L=2K, 8K and 32K, the differential at 8K and 32K (on
+                  by default; --no-sweep skips it);
   memory          peak device memory of one isolated layer at L = 2K, 8K, 32K: q, k, v and
                   out, and the drop in free device memory across the launches (0: the
                   library allocates nothing);
@@ -432,8 +434,9 @@ def main(argv=None) -> int:
                     help="skip the memory and placement-arm sections (profiling runs, as "
                          "for --no-gqa)")
     ap.add_argument("--no-sweep", action="store_true",
-                    help="skip the other lengths of Table 3 (full at L=2K/32K, differential at "
-                         "L=32K), which run by default; for profiling runs")
+                    help="skip the single-type layers at the lengths of Table 3 (full at "
+                         "L=2K/8K/32K, differential at L=8K/32K), which run by default; for "
+                         "profiling runs")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="host only: write the HBM traffic summary from two rocprofv3 "
                          "counter files and exit")
@@ -524,6 +527,7 @@ def main(argv=None) -> int:
     def step(events=None):
         mixer.mixer_stack_prefill(3, sched, qs, ks, vs, outs, W, lam, events=events)
 
+    gc.collect()
     settle(step, args.settle)
     for _ in range(args.warmup):
         step()
@@ -537,12 +541,19 @@ def main(argv=None) -> int:
         for e in evs:
             e.record()  # creates the events; the library re-records them on the stream
     torch.cuda.synchronize()
+    # One untimed pass of the timed loop itself, with the same events. The first pass of a
+    # freshly set-up loop runs every kernel 4-5 % slower than all later ones, measured with
+    # and without per-layer events and after clock settling or a continuous burst alike (the
+    # cause lies outside the kernels); the timed pass measures the steady state.
+    for i in range(K):
+        step(layer_events[i])
+    torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     # A full collection of Python's cyclic garbage takes milliseconds in a process that has
-    # torch loaded, and the argument arrays each step builds can trigger one: collect now and
-    # hold the collector off until the device has finished.
-    gc.collect()
+    # torch loaded, and the argument arrays each step builds can trigger one: the collector
+    # is held off until the device has finished (the collection itself runs before the clock
+    # settling: measured, the kernels ran 6 % slower in a timed region that followed it).
     gc.disable()
     try:
         t_wall = time.perf_counter()
@@ -573,6 +584,13 @@ def main(argv=None) -> int:
             + [layer_events[-1][n_layers].elapsed_time(end)])
     outside_layers = {"ms_total": round(sum(gaps), 5), "ms_max": round(max(gaps), 5),
                       "max_before_step": gaps.index(max(gaps))}
+    # Each depth of the stack on its own (median over the timed steps): a layer's cost next
+    # to neighbours of other types.
+    per_position = []
+    for layer in range(n_layers):
+        ts = sorted(evs[layer].elapsed_time(evs[layer + 1]) for evs in layer_events)
+        per_position.append({"variant": VARIANT_NAMES[sched[layer]],
+                             "ms_median": round(ts[len(ts) // 2], 5)})
     per_variant = {}
     for name, ts in per_launch.items():
         if not ts:
@@ -654,23 +672,30 @@ def main(argv=None) -> int:
     else:
         settle(step, args.settle)
     rounds = 10
-    arm_ev = {arm: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    # Events around every layer (recorded by the library on the launch stream).
+    arm_ev = {arm: [[torch.cuda.Event(enable_timing=True) for _ in range(n_layers + 1)]
                     for _ in range(rounds)] for arm in arm_orders}
+    for evl in arm_ev.values():
+        for evs in evl:
+            for e in evs:
+                e.record()  # creates the events; the library re-records them
     for arm, order in arm_orders.items():
         mixer.mixer_layers_prefill(order, qs, ks, vs, outs, W, lam)
     for r in range(rounds):
         for arm, order in arm_orders.items():
-            e0, e1 = arm_ev[arm][r]
-            e0.record()
-            mixer.mixer_layers_prefill(order, qs, ks, vs, outs, W, lam)
-            e1.record()
+            mixer.mixer_layers_prefill(order, qs, ks, vs, outs, W, lam, events=arm_ev[arm][r])
     torch.cuda.synchronize()
     arms = {}
     for arm, order in arm_orders.items():
-        ms = sum(e0.elapsed_time(e1) for e0, e1 in arm_ev[arm]) / rounds
+        ms = sum(evs[0].elapsed_time(evs[-1]) for evs in arm_ev[arm]) / rounds
         fl = sum(useful_flops(VARIANT_NAMES[v], B, H, L, d, W) for v in order)
+        pos = []
+        for layer in range(n_layers):
+            ts = sorted(evs[layer].elapsed_time(evs[layer + 1]) for evs in arm_ev[arm])
+            pos.append(round(ts[len(ts) // 2], 5))
         arms[arm] = {"order": "".join("FSD"[v] for v in order), "ms_per_step": round(ms, 5),
-                     "useful_tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
+                     "useful_tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                     "ms_median_per_layer": pos}
 
     # The matrix-core ceiling under the power cap (a measurement aid): the same bf16 MFMA on
     # random operands and nothing else, every SIMD busy, so that the prefill kernels can also
@@ -738,8 +763,10 @@ def main(argv=None) -> int:
     sweep = None
     if not args.no_sweep:
         sweep = {}
-        for name, variant, Ls in (("full", "full", (2048, 32768)),
-                                  ("differential", "differential", (32768,))):
+        # Each layer alone, back to back (the same workload as the stack's layers at
+        # L=8192, without the neighbours of other types).
+        for name, variant, Ls in (("full", "full", (2048, 8192, 32768)),
+                                  ("differential", "differential", (8192, 32768))):
             for Lx in Ls:
                 inp = synth.make_qkv(3 if variant == "full" else 4, B, H, Lx, d, "bf16")
                 t = [torch.from_numpy(b).view(torch.bfloat16).to(dev)
@@ -796,6 +823,7 @@ def main(argv=None) -> int:
         },
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "per_variant": per_variant,
+        "per_position": per_position,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "wall_s_timed": round(t_wall, 4),

@@ -84,6 +84,32 @@ def test_repeated_launches_and_two_streams_agree_bitwise(torch_cuda, variant):
         assert torch.equal(o.view(torch.int16), ref.view(torch.int16)), f"launch {i}"
 
 
+@pytest.mark.parametrize("variant", ["full", "differential"])
+def test_graph_replays_agree_bitwise(torch_cuda, variant):
+    # A captured persistent launch keeps its capture stream's queue slot; every replay must
+    # find the counters back at zero. Replays alternate with eager launches (on the current
+    # stream's own slot) and synchronisations, and each is checked against the eager result.
+    torch = torch_cuda
+    from heterogeneous_attention_mixer_amd import mixer as M
+    B, H, L, d = 1, 16, 8192, 128
+    q, k, v = device_tensors(make(8, B, H, L, d))
+    ref = run_layer((q, k, v), variant, 0, _lam(variant))
+    out = torch.full_like(q, float("nan"))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        M.mixer_prefill_async(q, k, v, out, variant, 0, _lam(variant))
+    other = torch.full_like(q, float("nan"))
+    for i in range(3):
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {i}"
+        other.fill_(float("nan"))
+        M.mixer_prefill_async(q, k, v, other, variant, 0, _lam(variant))
+        torch.cuda.synchronize()
+        assert torch.equal(other.view(torch.int16), ref.view(torch.int16)), f"eager {i}"
+
+
 def test_streams_beyond_the_queue_slots_fall_back(torch_cuda):
     # More streams than queue slots (256 per device): the later streams get the
     # one-workgroup-per-unit launch, which must give the same bits. The streams are made
