@@ -14,7 +14,7 @@ Reported (one JSON line):
                   query-key pair, summed over the nine layers, / step time);
   per_position    each of the nine layers' median time, in schedule order;
   per_variant     per-layer kernel time and useful TFLOP/s of each variant at L=8K, from HIP
-                  events recorded between the launches inside the timed steps, and the
+                  events recorded between the launches in a second pass of K steps, and the
                   fraction of the dense bf16 MFMA peak; the executed rate counts the matrix
                   instructions of the kernel's own tile schedule (masked keys of whole tiles,
                   the differential's second value product); the matrix-pipe busy share and
@@ -533,23 +533,35 @@ def main(argv=None) -> int:
         step()
     torch.cuda.synchronize()
 
-    # Timed region: K steps, each with HIP events around every layer launch.
+    # Timed region: K steps, bracketed by two HIP events that the library records on the
+    # launch stream right before the first layer and right after the last (so no host time
+    # before the first launch is counted, and no event sits between the layers). A second,
+    # instrumented pass of K steps then records an event around every layer for the
+    # per-layer figures; those records cost the stream a few microseconds each.
     K = args.steps
-    layer_events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_layers + 1)]
-                    for _ in range(K)]
-    for evs in layer_events:
-        for e in evs:
-            e.record()  # creates the events; the library re-records them on the stream
-    torch.cuda.synchronize()
-    # One untimed pass of the timed loop itself, with the same events. The first pass of a
-    # freshly set-up loop runs every kernel 4-5 % slower than all later ones, measured with
-    # and without per-layer events and after clock settling or a continuous burst alike (the
-    # cause lies outside the kernels); the timed pass measures the steady state.
-    for i in range(K):
-        step(layer_events[i])
-    torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    layer_events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_layers + 1)]
+                    for _ in range(K)]
+    for e in [start, end] + [e for evs in layer_events for e in evs]:
+        e.record()  # creates the events; the library re-records them on the stream
+    torch.cuda.synchronize()
+
+    def timed_pass():
+        for i in range(K):
+            evs = [None] * (n_layers + 1)
+            if i == 0:
+                evs[0] = start
+            if i == K - 1:
+                evs[n_layers] = end
+            step(evs)
+        torch.cuda.synchronize()
+
+    # One untimed pass of the timed loop itself first. The first pass of a freshly set-up
+    # loop runs every kernel a few % slower than all later ones, measured with and without
+    # per-layer events and after clock settling or a continuous burst alike (the cause lies
+    # outside the kernels); the timed pass measures the steady state.
+    timed_pass()
     # A full collection of Python's cyclic garbage takes milliseconds in a process that has
     # torch loaded, and the argument arrays each step builds can trigger one: the collector
     # is held off until the device has finished (the collection itself runs before the clock
@@ -557,11 +569,7 @@ def main(argv=None) -> int:
     gc.disable()
     try:
         t_wall = time.perf_counter()
-        start.record()
-        for i in range(K):
-            step(layer_events[i])
-        end.record()
-        torch.cuda.synchronize()
+        timed_pass()
         t_wall = time.perf_counter() - t_wall
     finally:
         gc.enable()
@@ -570,22 +578,17 @@ def main(argv=None) -> int:
     total_flops = sum(useful_flops(VARIANT_NAMES[v], B, H, L, d, W) for v in sched)
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
+    # The instrumented pass.
+    for i in range(K):
+        step(layer_events[i])
+    torch.cuda.synchronize()
     per_launch = {name: [] for name in VARIANT_NAMES}
     for evs in layer_events:
         for layer in range(n_layers):
             per_launch[VARIANT_NAMES[sched[layer]]].append(
                 evs[layer].elapsed_time(evs[layer + 1]))
-    # Device time in the timed region outside every layer's events: before the first layer,
-    # between steps and after the last. Near zero when the host keeps the queue full; a
-    # large figure means the device waited on the host (the value still counts it).
-    gaps = ([start.elapsed_time(layer_events[0][0])]
-            + [layer_events[i][n_layers].elapsed_time(layer_events[i + 1][0])
-               for i in range(K - 1)]
-            + [layer_events[-1][n_layers].elapsed_time(end)])
-    outside_layers = {"ms_total": round(sum(gaps), 5), "ms_max": round(max(gaps), 5),
-                      "max_before_step": gaps.index(max(gaps))}
-    # Each depth of the stack on its own (median over the timed steps): a layer's cost next
-    # to neighbours of other types.
+    # Each depth of the stack on its own (median over the instrumented steps): a layer's cost
+    # next to neighbours of other types.
     per_position = []
     for layer in range(n_layers):
         ts = sorted(evs[layer].elapsed_time(evs[layer + 1]) for evs in layer_events)
@@ -779,13 +782,18 @@ def main(argv=None) -> int:
                 # (34 us at L=2048) waits neither for the Python binding's per-call work
                 # between launches nor for its argument setup before the first.
                 reps = 10 if Lx <= 8192 else 3
-                evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-                for e in evs:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                for e in (e0, e1):
                     e.record()  # creates the events; the library re-records them
-                mixer.mixer_layers_prefill([variant] * reps, [t[0]] * reps, [t[1]] * reps,
-                                           [t[2]] * reps, [o] * reps, 0, lam, events=evs)
-                torch.cuda.synchronize()
-                ms = evs[0].elapsed_time(evs[-1]) / reps
+                # events only before the first launch and after the last; an untimed pass
+                # with the same events first, as for the stack
+                for _ in range(2):
+                    mixer.mixer_layers_prefill([variant] * reps, [t[0]] * reps,
+                                               [t[1]] * reps, [t[2]] * reps, [o] * reps, 0,
+                                               lam, events=[e0] + [None] * (reps - 1) + [e1])
+                    torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / reps
                 fl = useful_flops(variant, B, H, Lx, d, 0)
                 ex = executed_flops(variant, B, H, Lx, d, 0)
                 sweep[f"{name}_L{Lx}"] = {
@@ -827,7 +835,6 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "wall_s_timed": round(t_wall, 4),
-        "timed_outside_layers": outside_layers,
     }
     line["memory"] = memory
     line["arms"] = arms or None

@@ -156,18 +156,16 @@ int mixer_layers_prefill(int n, const int* variants, const void* const* q,
     if (rc != MIXER_OK) return rc;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (layer_events) {
-    for (int l = 0; l <= n; ++l)
-      if (!layer_events[l]) return MIXER_EINVAL;
-    if (hipEventRecord(static_cast<hipEvent_t>(layer_events[0]), s) != hipSuccess)
-      return MIXER_EHIP;
-  }
+  // Records event i where the caller asked for one (a NULL entry records nothing).
+  auto mark = [&](int i) {
+    return !layer_events || !layer_events[i] ||
+           hipEventRecord(static_cast<hipEvent_t>(layer_events[i]), s) == hipSuccess;
+  };
+  if (!mark(0)) return MIXER_EHIP;
   for (int l = 0; l < n; ++l) {
     const int rc = launch(layers[(size_t)l], stream);
     if (rc != MIXER_OK) return rc;
-    if (layer_events &&
-        hipEventRecord(static_cast<hipEvent_t>(layer_events[l + 1]), s) != hipSuccess)
-      return MIXER_EHIP;
+    if (!mark(l + 1)) return MIXER_EHIP;
   }
   return MIXER_OK;
 }

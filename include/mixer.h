@@ -144,7 +144,8 @@ int mixer_latin_check(int N, const int *sched);
  * q, k, v, out    host arrays of N*N device pointers, one [B, H, L, d] bf16 tensor each.
  * window, lambda  used by the SLIDING and DIFFERENTIAL layers respectively.
  * layer_events    NULL, or a host array of N*N + 1 hipEvent_t (passed as void*): event 0
- *                 is recorded before layer 0 and event l + 1 after layer l.
+ *                 is recorded before layer 0 and event l + 1 after layer l; a NULL entry
+ *                 records nothing there (each record costs the stream a few microseconds).
  * Every layer's arguments are validated before the first launch. Returns MIXER_OK,
  * MIXER_ENOTLATIN (schedule not Latin; nothing launched), the first invalid layer's
  * validation error (nothing launched), or MIXER_EHIP as mixer_layers_prefill reports it.
