@@ -49,7 +49,9 @@
 //     a rare path at the start of the next matrix phase, taken only while a row has no
 //     reference or when a row's tile sum exceeds 2^8.
 //   * Work order: heaviest query tiles first (sliding: the short first-window tiles first);
-//     all tiles of a head on one XCD when B*H is a multiple of 8.
+//     all tiles of a head on one XCD when B*H is a multiple of 8. The phase-separated
+//     kernel launches persistent when it has more units than CUs: one workgroup per CU takes
+//     units from per-XCD queues in that order and steals from the other queues at the end.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -1184,10 +1186,10 @@ hipError_t launch_phase(const PrefillLaunch& a, int nq, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Full causal takes the phase-separated kernel (256-row workgroups, one per CU) when its
-// grid is more than one workgroup per CU, so that the later workgroups fill in behind the
-// heavy first ones; on smaller grids the pipelined kernel's two 128-row workgroups per CU
-// (or its key split) balance the causal work better.
+// Full causal takes the phase-separated kernel (256-row units, one workgroup per CU) when it
+// has more units than CUs, so that the later, lighter units fill in behind the heavy first
+// ones; with fewer, the pipelined kernel's two 128-row workgroups per CU (or its key split)
+// balance the causal work better.
 template <int D>
 hipError_t launch_full(const PrefillLaunch& a, hipStream_t stream) {
   constexpr int BM = PhaseShape<kFull>::bm;
