@@ -56,8 +56,8 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <thread>
 #include <type_traits>
-#include <utility>
 #include <vector>
 
 #include "device_common.h"
@@ -1150,19 +1150,28 @@ hipError_t launch_dma_t(const PrefillLaunch& a, hipStream_t stream) {
 // The queue slot of (device, stream): the stream's rank among the streams of that device
 // that have launched the persistent kernel, or -1 once every slot has an owner. Launches on
 // one stream run in order, so they share its slot safely; a slot never passes to another
-// stream. A graph captured from a stream keeps that stream's slot.
+// stream. The per-thread default stream is one handle for a different stream in every host
+// thread, so it is told apart by thread. A graph captured from a stream keeps that stream's
+// slot.
 int queue_slot(int dev, hipStream_t stream) {
+  struct Owner {
+    int dev;
+    hipStream_t stream;
+    std::thread::id thread;
+  };
   static std::mutex mu;
-  static std::vector<std::pair<int, hipStream_t>> owners;
+  static std::vector<Owner> owners;
+  const std::thread::id thread =
+      stream == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id();
   std::lock_guard<std::mutex> hold(mu);
   int n = 0;
-  for (const auto& o : owners) {
-    if (o.first != dev) continue;
-    if (o.second == stream) return n;
+  for (const Owner& o : owners) {
+    if (o.dev != dev) continue;
+    if (o.stream == stream && o.thread == thread) return n;
     ++n;
   }
   if (n >= kQueueSlots) return -1;
-  owners.emplace_back(dev, stream);
+  owners.push_back(Owner{dev, stream, thread});
   return n;
 }
 

@@ -110,6 +110,45 @@ def test_graph_replays_agree_bitwise(torch_cuda, variant):
         assert torch.equal(other.view(torch.int16), ref.view(torch.int16)), f"eager {i}"
 
 
+def test_per_thread_default_streams_of_two_threads_agree_bitwise(torch_cuda):
+    # The per-thread default stream is one handle for a different stream in each host
+    # thread; two threads launching on it at once must not share queue counters.
+    import ctypes
+    import threading
+    torch = torch_cuda
+    from heterogeneous_attention_mixer_amd import mixer as M
+    B, H, L, d = 1, 16, 8192, 128
+    q, k, v = device_tensors(make(9, B, H, L, d))
+    ref = run_layer((q, k, v), "full", 0, 0.0)
+    outs = [[torch.full_like(q, float("nan")) for _ in range(4)] for _ in range(2)]
+    torch.cuda.synchronize()
+    per_thread = ctypes.c_void_p(2)  # hipStreamPerThread
+    errs = []
+
+    def launch(mine):
+        try:
+            torch.cuda.set_device(0)
+            for o in mine:
+                rc = M.lib().mixer_prefill_async(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                 o.data_ptr(), 0, 0, 0.0, B, H, L, d,
+                                                 per_thread)
+                if rc != 0:
+                    errs.append(rc)
+        except Exception as e:  # reported below
+            errs.append(e)
+
+    threads = [threading.Thread(target=launch, args=(outs[i],)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errs, errs
+    for i, mine in enumerate(outs):
+        for j, o in enumerate(mine):
+            assert torch.equal(o.view(torch.int16), ref.view(torch.int16)), f"thread {i} {j}"
+
+
 def test_streams_beyond_the_queue_slots_fall_back(torch_cuda):
     # More streams than queue slots (256 per device): the later streams get the
     # one-workgroup-per-unit launch, which must give the same bits. The streams are made
