@@ -225,7 +225,8 @@ def _layer_args(m, variants, qs, ks, vs, outs, events):
     if events is not None:
         if len(events) != m + 1:
             raise MixerError("events must hold one entry per layer plus one", EINVAL)
-        ev = (ctypes.c_void_p * (m + 1))(*[None if e is None else e.cuda_event
+        ev = (ctypes.c_void_p * (m + 1))(*[None if e is None else
+                                           e if isinstance(e, int) else e.cuda_event
                                            for e in events])
     return (B, H, L, d), s, arr(qs), arr(ks), arr(vs), arr(outs), ev
 
@@ -234,8 +235,9 @@ def mixer_stack_prefill(n: int, sched, qs, ks, vs, outs, window: int = 0, lam: f
                         events=None, stream=None):
     """Runs the n*n layers of a Latin schedule back to back on one stream. ``qs`` .. ``outs``
     are sequences of n*n bf16 tensors of one shape; ``events`` optionally n*n + 1 entries,
-    each a recorded ``torch.cuda.Event`` that the library re-records at that point (before
-    layer 0, after each layer) or None to record nothing there."""
+    each an event that the library records at that point (before layer 0, after each layer):
+    a created ``torch.cuda.Event``, an object with a ``cuda_event`` handle, or a raw
+    hipEvent_t as an int; or None to record nothing there."""
     import torch
     (B, H, L, d), s, q, k, v, o, ev = _layer_args(n * n, sched, qs, ks, vs, outs, events)
     st = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_of(qs[0])
