@@ -610,6 +610,7 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
 // phases strictly alternate, so one set of score and probability registers is enough.
 // K[k] and V[k-1] (the pair of tile k) live in LDS buffer pair k mod 4; the loads of pair
 // k+3 are issued in the V phase of tile k.
+
 // Work queues of the persistent launch. A slot holds one counter per XCD queue (each on a
 // 64-byte line of its own) and a count of the workgroups that have finished; the last
 // workgroup to finish sets them all back to zero, so a slot is clean between launches. The
@@ -732,7 +733,7 @@ prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ k
     for (int e = 0; e < 8; ++e) rsel[e] = one ? (__bf16)1.0f : (__bf16)0.0f;
   }
 
-  // Units: (head, query tile) pairs. With the head count a multiple of 8 there is one queue
+  // Units: (batch x head, query tile) pairs. With B*H a multiple of 8 there is one queue
   // per XCD, holding that XCD's heads heaviest tile first (the order map_unit deals them);
   // otherwise one queue. Workgroup b starts on ticket b / nQ of queue b % nQ (its XCD's, as
   // the hardware deals workgroups to the XCDs round-robin). With a slot (the persistent
@@ -749,359 +750,359 @@ prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ k
   }
   __syncthreads();
   for (;;) {
-  int bh, qt;
-  {
-    const int BHu = rfl(ua.BH), nqu = rfl(ua.nq);
-    const int nQ = ((BHu & 7) == 0) ? kQueues : 1;
-    map_unit(rfl(ua.ut) * nQ + rfl(ua.ux), BHu, nqu, &bh, &qt);
-  }
-  const int q0 = qt * BM;
-  const int qw = q0 + rb * 32;
-  const int qi = qw + lr;
-  const size_t head = (size_t)bh * (size_t)L * D;
-  const size_t kv_head = (size_t)(bh / rfl(ua.G)) * (size_t)L * D;
-  const __amdgpu_buffer_rsrc_t Qr = make_rsrc(rfl_ptr(ua.q) + head, head_bytes);
-  const unsigned long long Kbase = reinterpret_cast<unsigned long long>(rfl_ptr(ua.k) + kv_head);
-  const unsigned long long Vbase = reinterpret_cast<unsigned long long>(rfl_ptr(ua.v) + kv_head);
-
-  bf16x8 qf[NQ];
-#pragma unroll
-  for (int kk = 0; kk < NQ; ++kk) qf[kk] = bload8<__bf16>(Qr, qi * D + ch0 + kk * 16 + lg * 8);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-
-  const int q_last = min(q0 + BM, L) - 1;
-  const int lo = 0;
-  const int hi = q_last / BN;
-
-  auto load_tile = [&](bool v, int dst, int j) {
-    const u32x4 r = rsrc_words((v ? Vbase : Kbase) + (unsigned long long)j * TILEB,
-                               head_bytes - j * TILEB);
-    // The LDS destination is formed here, behind an empty statement: left visible, the
-    // compiler keeps every buffer pair's destinations live across the unrolled key loop and
-    // runs out of scalar registers.
-    unsigned m0b = lds_addr + (unsigned)wave_s * 1024u + (unsigned)dst;
-    asm volatile("" : "+s"(m0b));
-#pragma unroll
-    for (int t = 0; t < NIW; ++t)
-      lds_load16(r, m0b + (unsigned)(t * kWaves * 1024), ld_off[t]);
-  };
-  // Does every row of the wave see every key of tile j?
-  auto full_tile = [&](int j) { return j * BN + BN - 1 <= qw; };
-
-  floatx16 o[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-  float m = -INFINITY, l = 0.0f;
-  float lt = 0.0f;  // the row's sum of the last tile's probabilities, not yet in l
-  floatx16 s[2];
-  bf16x8 p[2][2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) p[kb][h][e] = (__bf16)0.0f;
-
-  // Probabilities exp2(c (s - m)) of the tile against the current reference, rounded to
-  // bf16 into p; the row's sum of the rounded values into lt, on the matrix core.
-  auto take_exps = [&]() {
-    const float mc = (m == -INFINITY) ? 0.0f : m * c;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          p[kb][h][e] = (__bf16)fast_exp2(__builtin_fmaf(s[kb][h * 8 + e], c, -mc));
-    // The partner wave is in its M phase at raised priority, so at the base priority these
-    // four would wait for gaps in its matrix stream (about 240 cycles of the V phase): they
-    // take the same priority and interleave with it instead.
-    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rsel, p[kb][h], acc, 0, 0, 0);
-    __builtin_amdgcn_s_setprio(0);
-    lt = acc[0];
-  };
-  // Reference test for the tile whose probabilities the V phase just took (S still holds
-  // its masked scores). While a row has no reference yet, or when a row's tile sum says a
-  // probability may exceed 2^gap, the row max moves the reference, l and O follow (O holds
-  // the tiles before this one), and the probabilities are taken again. Then l takes lt.
-  auto settle = [&]() {
-    if (__any((lt > kTileSumBound) | (m == -INFINITY))) {
-      float t0 = vmax3(s[0][0], s[0][1], s[0][2]);
-      float t1 = vmax3(s[1][0], s[1][1], s[1][2]);
-#pragma unroll
-      for (int r = 3; r < 15; r += 2) {
-        t0 = vmax3(t0, s[0][r], s[0][r + 1]);
-        t1 = vmax3(t1, s[1][r], s[1][r + 1]);
-      }
-      const float tmax = xhalf_max(vmax3(vmax3(t0, s[0][15], t1), s[1][15], s[1][15]));
-      const float m_new = __builtin_fmaxf(m, tmax);
-      if (m_new != m) {
-        const float alpha = (m == -INFINITY) ? 0.0f : fast_exp2((m - m_new) * c);
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-        m = m_new;
-        take_exps();
-      }
+    int bh, qt;
+    {
+      const int BHu = rfl(ua.BH), nqu = rfl(ua.nq);
+      const int nQ = ((BHu & 7) == 0) ? kQueues : 1;
+      map_unit(rfl(ua.ut) * nQ + rfl(ua.ux), BHu, nqu, &bh, &qt);
     }
-    l += lt;
-  };
-  // M phase of tile k (pair buffer `pb`, a compile-time constant, so that every operand
-  // read's LDS offset is an instruction immediate): S = K[k] Q^T; O += V[k-1] P.
-  auto m_phase = [&](auto pb_c) {
-    constexpr int pb = decltype(pb_c)::value;
-    constexpr int kbase = pb * TILEB;
-    int ka[NQ], va[DB][2];
+    const int q0 = qt * BM;
+    const int qw = q0 + rb * 32;
+    const int qi = qw + lr;
+    const size_t head = (size_t)bh * (size_t)L * D;
+    const size_t kv_head = (size_t)(bh / rfl(ua.G)) * (size_t)L * D;
+    const __amdgpu_buffer_rsrc_t Qr = make_rsrc(rfl_ptr(ua.q) + head, head_bytes);
+    const unsigned long long Kbase = reinterpret_cast<unsigned long long>(rfl_ptr(ua.k) + kv_head);
+    const unsigned long long Vbase = reinterpret_cast<unsigned long long>(rfl_ptr(ua.v) + kv_head);
+
+    bf16x8 qf[NQ];
 #pragma unroll
-    for (int kk = 0; kk < NQ; ++kk) ka[kk] = k_off[kk] + kbase;
+    for (int kk = 0; kk < NQ; ++kk) qf[kk] = bload8<__bf16>(Qr, qi * D + ch0 + kk * 16 + lg * 8);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+
+    const int q_last = min(q0 + BM, L) - 1;
+    const int lo = 0;
+    const int hi = q_last / BN;
+
+    auto load_tile = [&](bool v, int dst, int j) {
+      const u32x4 r = rsrc_words((v ? Vbase : Kbase) + (unsigned long long)j * TILEB,
+                                 head_bytes - j * TILEB);
+      // The LDS destination is formed here, behind an empty statement: left visible, the
+      // compiler keeps every buffer pair's destinations live across the unrolled key loop and
+      // runs out of scalar registers.
+      unsigned m0b = lds_addr + (unsigned)wave_s * 1024u + (unsigned)dst;
+      asm volatile("" : "+s"(m0b));
+#pragma unroll
+      for (int t = 0; t < NIW; ++t)
+        lds_load16(r, m0b + (unsigned)(t * kWaves * 1024), ld_off[t]);
+    };
+    // Does every row of the wave see every key of tile j?
+    auto full_tile = [&](int j) { return j * BN + BN - 1 <= qw; };
+
+    floatx16 o[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int rr = 0; rr < 2; ++rr) va[db][rr] = v_off[db][rr] + kbase;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < NQ; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-            lds + ka[kk] + kb * 32 * ROWB);
-        s[kb] = mfma32(a, qf[kk], s[kb]);
-      }
+      for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+    float m = -INFINITY, l = 0.0f;
+    float lt = 0.0f;  // the row's sum of the last tile's probabilities, not yet in l
+    floatx16 s[2];
+    bf16x8 p[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int roff = (kb * 32 + 16 * h) * ROWB;
-          const shortx4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              reinterpret_cast<__attribute__((address_space(3))) shortx4*>(
-                  lds + va[db][0] + roff));
-          const shortx4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              reinterpret_cast<__attribute__((address_space(3))) shortx4*>(
-                  lds + va[db][1] + roff));
-          const bf16x8 a = __builtin_bit_cast(
-              bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[db] = mfma32(a, p[kb][h], o[db]);
-        }
-    // Operand reads ahead of the matrix instructions that use them. A score MFMA reads one
-    // K operand, a value MFMA two V reads: kEarly reads after each score MFMA (three for the
-    // differential's 8 score MFMAs, two for full's 16) put the value product's reads well
-    // ahead when it starts, and one read after each of its first value MFMAs keeps them
-    // ahead to the end of the phase (an even 1.5 reads per MFMA let the lead fall to one
-    // MFMA, less than the LDS latency).
-    constexpr int kEarly = kDiff ? 3 : 2;
-    constexpr int kLate = 2 * NQ + 8 * DB - 4 - 2 * NQ * kEarly;  // reads for value MFMAs
-    static_assert(kLate >= 0 && kLate <= 4 * DB, "read schedule");
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * NQ; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, kEarly, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < kLate; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * DB - kLate, 0);
-  };
-  // V phase of tile k: loads of pair k+3, then the probabilities of S (masked on tiles
-  // that cross the diagonal) against the current reference.
-  auto v_phase = [&](int k) {
-    const int nb = ((k + 3 - lo) & 3) * TILEB;
-    load_tile(false, nb, k + 3);
-    load_tile(true, 4 * TILEB + nb, k + 2);
-    if (!full_tile(k)) {
-      // Element (kb, r) holds key k*BN + cc + 4*lg with cc a compile-time constant: visible
-      // when cc <= qi - k*BN - 4*lg.
-      const int t = qi - k * BN - 4 * lg;
+        for (int e = 0; e < 8; ++e) p[kb][h][e] = (__bf16)0.0f;
+
+    // Probabilities exp2(c (s - m)) of the tile against the current reference, rounded to
+    // bf16 into p; the row's sum of the rounded values into lt, on the matrix core.
+    auto take_exps = [&]() {
+      const float mc = (m == -INFINITY) ? 0.0f : m * c;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kb * 32 + 8 * (r >> 2) + (r & 3) > t) s[kb][r] = -INFINITY;
-    }
-    // The first tile's rows have no reference yet, so the next M phase's test always takes
-    // its rare path, which takes the exponentials and sums again: none here.
-    if (k > lo) take_exps();
-  };
-
-  // ---- prologue (lo is tile 0): pair 0 = (K[0], zeros), pair 1 = (K[1], V[0]),
-  // pair 2 = (K[2], V[1]).
-  {
-    const floatx4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-    floatx4* const vz = reinterpret_cast<floatx4*>(smem + 4 * TILEB);
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int i = tid; i < TILEB / 16; i += kWaves * kWave) vz[i] = z;
-  }
-  load_tile(false, 0 * TILEB, lo);
-  load_tile(false, 1 * TILEB, lo + 1);
-  load_tile(true, 5 * TILEB, lo);
-  load_tile(false, 2 * TILEB, lo + 2);
-  load_tile(true, 6 * TILEB, lo + 1);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();
+          for (int e = 0; e < 8; ++e)
+            p[kb][h][e] = (__bf16)fast_exp2(__builtin_fmaf(s[kb][h * 8 + e], c, -mc));
+      // The partner wave is in its M phase at raised priority, so at the base priority these
+      // four would wait for gaps in its matrix stream (about 240 cycles of the V phase): they
+      // take the same priority and interleave with it instead.
+      floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rsel, p[kb][h], acc, 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
+      lt = acc[0];
+    };
+    // Reference test for the tile whose probabilities the V phase just took (S still holds
+    // its masked scores). While a row has no reference yet, or when a row's tile sum says a
+    // probability may exceed 2^gap, the row max moves the reference, l and O follow (O holds
+    // the tiles before this one), and the probabilities are taken again. Then l takes lt.
+    auto settle = [&]() {
+      if (__any((lt > kTileSumBound) | (m == -INFINITY))) {
+        float t0 = vmax3(s[0][0], s[0][1], s[0][2]);
+        float t1 = vmax3(s[1][0], s[1][1], s[1][2]);
+#pragma unroll
+        for (int r = 3; r < 15; r += 2) {
+          t0 = vmax3(t0, s[0][r], s[0][r + 1]);
+          t1 = vmax3(t1, s[1][r], s[1][r + 1]);
+        }
+        const float tmax = xhalf_max(vmax3(vmax3(t0, s[0][15], t1), s[1][15], s[1][15]));
+        const float m_new = __builtin_fmaxf(m, tmax);
+        if (m_new != m) {
+          const float alpha = (m == -INFINITY) ? 0.0f : fast_exp2((m - m_new) * c);
+          l *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+          m = m_new;
+          take_exps();
+        }
+      }
+      l += lt;
+    };
+    // M phase of tile k (pair buffer `pb`, a compile-time constant, so that every operand
+    // read's LDS offset is an instruction immediate): S = K[k] Q^T; O += V[k-1] P.
+    auto m_phase = [&](auto pb_c) {
+      constexpr int pb = decltype(pb_c)::value;
+      constexpr int kbase = pb * TILEB;
+      int ka[NQ], va[DB][2];
+#pragma unroll
+      for (int kk = 0; kk < NQ; ++kk) ka[kk] = k_off[kk] + kbase;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) va[db][rr] = v_off[db][rr] + kbase;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < NQ; ++kk)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+              lds + ka[kk] + kb * 32 * ROWB);
+          s[kb] = mfma32(a, qf[kk], s[kb]);
+        }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const int roff = (kb * 32 + 16 * h) * ROWB;
+            const shortx4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                reinterpret_cast<__attribute__((address_space(3))) shortx4*>(
+                    lds + va[db][0] + roff));
+            const shortx4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                reinterpret_cast<__attribute__((address_space(3))) shortx4*>(
+                    lds + va[db][1] + roff));
+            const bf16x8 a = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+            o[db] = mfma32(a, p[kb][h], o[db]);
+          }
+      // Operand reads ahead of the matrix instructions that use them. A score MFMA reads one
+      // K operand, a value MFMA two V reads: kEarly reads after each score MFMA (three for the
+      // differential's 8 score MFMAs, two for full's 16) put the value product's reads well
+      // ahead when it starts, and one read after each of its first value MFMAs keeps them
+      // ahead to the end of the phase (an even 1.5 reads per MFMA let the lead fall to one
+      // MFMA, less than the LDS latency).
+      constexpr int kEarly = kDiff ? 3 : 2;
+      constexpr int kLate = 2 * NQ + 8 * DB - 4 - 2 * NQ * kEarly;  // reads for value MFMAs
+      static_assert(kLate >= 0 && kLate <= 4 * DB, "read schedule");
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * NQ; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, kEarly, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < kLate; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * DB - kLate, 0);
+    };
+    // V phase of tile k: loads of pair k+3, then the probabilities of S (masked on tiles
+    // that cross the diagonal) against the current reference.
+    auto v_phase = [&](int k) {
+      const int nb = ((k + 3 - lo) & 3) * TILEB;
+      load_tile(false, nb, k + 3);
+      load_tile(true, 4 * TILEB + nb, k + 2);
+      if (!full_tile(k)) {
+        // Element (kb, r) holds key k*BN + cc + 4*lg with cc a compile-time constant: visible
+        // when cc <= qi - k*BN - 4*lg.
+        const int t = qi - k * BN - 4 * lg;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + 8 * (r >> 2) + (r & 3) > t) s[kb][r] = -INFINITY;
+      }
+      // The first tile's rows have no reference yet, so the next M phase's test always takes
+      // its rare path, which takes the exponentials and sums again: none here.
+      if (k > lo) take_exps();
+    };
 
-  // ---- key loop: group 1 runs one phase behind group 0; both run the same number of
-  // barriers. The last M phase (tile hi+1) only adds V[hi] P[hi]; its scores are discarded.
-  if (grp == 1) __syncthreads();
-  // The loop is unrolled by the four buffer pairs (tile k uses pair k mod 4; lo is 0 here).
-  auto step = [&](auto pb_c, int k) {
-    if (k > lo) settle();  // tile k-1
-    __builtin_amdgcn_s_setprio(1);
-    m_phase(pb_c);
-    __builtin_amdgcn_s_setprio(0);
-    __builtin_amdgcn_s_waitcnt(kWaitOlder);
-    __syncthreads();
-    if (k <= hi) v_phase(k);
-    __syncthreads();
-  };
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  using P2 = std::integral_constant<int, 2>;
-  using P3 = std::integral_constant<int, 3>;
-  int k = lo;
-  for (; k + 3 <= hi + 1; k += 4) {
-    step(P0{}, k);
-    step(P1{}, k + 1);
-    step(P2{}, k + 2);
-    step(P3{}, k + 3);
-  }
-  if (k <= hi + 1) step(P0{}, k++);
-  if (k <= hi + 1) step(P1{}, k++);
-  if (k <= hi + 1) step(P2{}, k++);
-  // The last M phase's scores are discarded; reading them here keeps the compiler from
-  // dropping them only where it can prove which step comes last (every workgroup then
-  // issues the same matrix work for its tile range).
-  asm volatile("" ::"v"(s[0]), "v"(s[1]));
-  // Group 0 ends its key loop one phase before group 1. Once its own tile loads are in, wave
-  // 0 asks for the next unit, so that the answer comes back while the workgroup finishes:
-  // lane 0 takes the next ticket of the current queue, and lanes 32.. read every queue's
-  // counter in the same round trip, for when the current queue turns out empty. With no
-  // tile load of the wave in flight, the key loop's counted waits are not disturbed.
-  unsigned tk_next = 0;
-  unsigned q_seen = 0;
-  if (grp == 0) {
+    // ---- prologue (lo is tile 0): pair 0 = (K[0], zeros), pair 1 = (K[1], V[0]),
+    // pair 2 = (K[2], V[1]).
+    {
+      const floatx4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+      floatx4* const vz = reinterpret_cast<floatx4*>(smem + 4 * TILEB);
+#pragma unroll
+      for (int i = tid; i < TILEB / 16; i += kWaves * kWave) vz[i] = z;
+    }
+    load_tile(false, 0 * TILEB, lo);
+    load_tile(false, 1 * TILEB, lo + 1);
+    load_tile(true, 5 * TILEB, lo);
+    load_tile(false, 2 * TILEB, lo + 2);
+    load_tile(true, 6 * TILEB, lo + 1);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    if (wave_s == 0 && ua.slot >= 0) {
-      unsigned* const qs = g_unit_queue + ua.slot * kSlotWords;
-      const int nQ = ((ua.BH & 7) == 0) ? kQueues : 1;
-      if (lane == 0)
-        tk_next = __hip_atomic_fetch_add(qs + 16 * ua.ux, 1u, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-      else if (lane >= 32 && lane < 32 + nQ)
-        q_seen = __hip_atomic_load(qs + 16 * (lane - 32), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+
+    // ---- key loop: group 1 runs one phase behind group 0; both run the same number of
+    // barriers. The last M phase (tile hi+1) only adds V[hi] P[hi]; its scores are discarded.
+    if (grp == 1) __syncthreads();
+    // The loop is unrolled by the four buffer pairs (tile k uses pair k mod 4; lo is 0 here).
+    auto step = [&](auto pb_c, int k) {
+      if (k > lo) settle();  // tile k-1
+      __builtin_amdgcn_s_setprio(1);
+      m_phase(pb_c);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_waitcnt(kWaitOlder);
+      __syncthreads();
+      if (k <= hi) v_phase(k);
+      __syncthreads();
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
+    using P3 = std::integral_constant<int, 3>;
+    int k = lo;
+    for (; k + 3 <= hi + 1; k += 4) {
+      step(P0{}, k);
+      step(P1{}, k + 1);
+      step(P2{}, k + 2);
+      step(P3{}, k + 3);
+    }
+    if (k <= hi + 1) step(P0{}, k++);
+    if (k <= hi + 1) step(P1{}, k++);
+    if (k <= hi + 1) step(P2{}, k++);
+    // The last M phase's scores are discarded; reading them here keeps the compiler from
+    // dropping them only where it can prove which step comes last (every workgroup then
+    // issues the same matrix work for its tile range).
+    asm volatile("" ::"v"(s[0]), "v"(s[1]));
+    // Group 0 ends its key loop one phase before group 1. Once its own tile loads are in, wave
+    // 0 asks for the next unit, so that the answer comes back while the workgroup finishes:
+    // lane 0 takes the next ticket of the current queue, and lanes 32.. read every queue's
+    // counter in the same round trip, for when the current queue turns out empty. With no
+    // tile load of the wave in flight, the key loop's counted waits are not disturbed.
+    unsigned tk_next = 0;
+    unsigned q_seen = 0;
+    if (grp == 0) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      if (wave_s == 0 && ua.slot >= 0) {
+        unsigned* const qs = g_unit_queue + ua.slot * kSlotWords;
+        const int nQ = ((ua.BH & 7) == 0) ? kQueues : 1;
+        if (lane == 0)
+          tk_next = __hip_atomic_fetch_add(qs + 16 * ua.ux, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+        else if (lane >= 32 && lane < 32 + nQ)
+          q_seen = __hip_atomic_load(qs + 16 * (lane - 32), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
+
+    // ---- epilogue. Element (db, r) of a lane is channel db*32 + 8*(r/4) + 4*lg + r%4 of
+    // query qi.
+    const float lsum = l;  // the row-sum MFMAs already add the two lanes of a query
+    if constexpr (!kDiff) {  // out = O / l
+      if (qi < L) {
+        const float inv = 1.0f / lsum;
+        __bf16* orow = rfl_ptr(ua.o) + head + (size_t)qi * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            store4(orow + db * 32 + 8 * r4 + 4 * lg, o[db][r4 * 4] * inv,
+                   o[db][r4 * 4 + 1] * inv, o[db][r4 * 4 + 2] * inv, o[db][r4 * 4 + 3] * inv);
+      }
+    } else {
+    // Differential: out = O1 / l1 - lambda * O2 / l2, map 1's term passed to map 0 through LDS.
+    __syncthreads();  // every wave is done reading the tiles
+    {
+      float* const xch = reinterpret_cast<float*>(smem) + rb * 64 * (DB * 16);
+      if (map == 1) {
+        const float sc = ua.lambda / lsum;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xch[(db * 16 + r) * 64 + lane] = o[db][r] * sc;
+      }
     }
     __syncthreads();
-  } else {
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  }
-
-  // ---- epilogue. Element (db, r) of a lane is channel db*32 + 8*(r/4) + 4*lg + r%4 of
-  // query qi.
-  const float lsum = l;  // the row-sum MFMAs already add the two lanes of a query
-  if constexpr (!kDiff) {  // out = O / l
-    if (qi < L) {
+    if (map == 0 && qi < L) {
       const float inv = 1.0f / lsum;
+      const float* const xch = reinterpret_cast<const float*>(smem) + rb * 64 * (DB * 16);
       __bf16* orow = rfl_ptr(ua.o) + head + (size_t)qi * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-          store4(orow + db * 32 + 8 * r4 + 4 * lg, o[db][r4 * 4] * inv,
-                 o[db][r4 * 4 + 1] * inv, o[db][r4 * 4 + 2] * inv, o[db][r4 * 4 + 3] * inv);
-    }
-  } else {
-  // Differential: out = O1 / l1 - lambda * O2 / l2, map 1's term passed to map 0 through LDS.
-  __syncthreads();  // every wave is done reading the tiles
-  {
-    float* const xch = reinterpret_cast<float*>(smem) + rb * 64 * (DB * 16);
-    if (map == 1) {
-      const float sc = ua.lambda / lsum;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          float x[4];
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) xch[(db * 16 + r) * 64 + lane] = o[db][r] * sc;
-    }
-  }
-  __syncthreads();
-  if (map == 0 && qi < L) {
-    const float inv = 1.0f / lsum;
-    const float* const xch = reinterpret_cast<const float*>(smem) + rb * 64 * (DB * 16);
-    __bf16* orow = rfl_ptr(ua.o) + head + (size_t)qi * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        float x[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[e] = o[db][r4 * 4 + e] * inv;
-          x[e] -= xch[(db * 16 + r4 * 4 + e) * 64 + lane];
+          for (int e = 0; e < 4; ++e) {
+            x[e] = o[db][r4 * 4 + e] * inv;
+            x[e] -= xch[(db * 16 + r4 * 4 + e) * 64 + lane];
+          }
+          store4(orow + db * 32 + 8 * r4 + 4 * lg, x[0], x[1], x[2], x[3]);
         }
-        store4(orow + db * 32 + 8 * r4 + 4 * lg, x[0], x[1], x[2], x[3]);
-      }
-  }
-  }
+    }
+    }
 
-  if (rfl(ua.slot) < 0) break;
-  // Wave 0 settles the next unit. When the current queue is empty it takes a ticket from the
-  // queue with the most left, by the counters read with the request (lanes 32..) and read
-  // again after every miss; a queue found empty stays empty, so this ends after at most nQ
-  // misses.
-  if (wave_s == 0) {
-    const int nQ = ((rfl(ua.BH) & 7) == 0) ? kQueues : 1;
-    const int Ux = rfl(ua.BH) * rfl(ua.nq) / nQ;
-    unsigned* const qslot = g_unit_queue + rfl(ua.slot) * kSlotWords;
-    // Tickets below this were dealt to the workgroups as their first units.
-    auto first_dyn = [&](int x) { return (rfl(ua.grid) - x + nQ - 1) / nQ; };
-    const int ux = rfl(ua.ux);
-    int nx = ux;
-    int nt = first_dyn(ux) + __builtin_amdgcn_readfirstlane((int)tk_next);
-    bool reread = false;
-    while (nt >= Ux) {
-      if (reread && lane >= 32 && lane < 32 + nQ)
-        q_seen = __hip_atomic_load(qslot + 16 * (lane - 32), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-      reread = true;
-      nx = -1;
-      int most = 0;
-      for (int x = 0; x < nQ; ++x) {
-        const int v = Ux - first_dyn(x) - (int)__builtin_amdgcn_readlane(q_seen, 32 + x);
-        if (v > most) {
-          most = v;
-          nx = x;
+    if (rfl(ua.slot) < 0) break;
+    // Wave 0 settles the next unit. When the current queue is empty it takes a ticket from the
+    // queue with the most left, by the counters read with the request (lanes 32..) and read
+    // again after every miss; a queue found empty stays empty, so this ends after at most nQ
+    // misses.
+    if (wave_s == 0) {
+      const int nQ = ((rfl(ua.BH) & 7) == 0) ? kQueues : 1;
+      const int Ux = rfl(ua.BH) * rfl(ua.nq) / nQ;
+      unsigned* const qslot = g_unit_queue + rfl(ua.slot) * kSlotWords;
+      // Tickets below this were dealt to the workgroups as their first units.
+      auto first_dyn = [&](int x) { return (rfl(ua.grid) - x + nQ - 1) / nQ; };
+      const int ux = rfl(ua.ux);
+      int nx = ux;
+      int nt = first_dyn(ux) + __builtin_amdgcn_readfirstlane((int)tk_next);
+      bool reread = false;
+      while (nt >= Ux) {
+        if (reread && lane >= 32 && lane < 32 + nQ)
+          q_seen = __hip_atomic_load(qslot + 16 * (lane - 32), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+        reread = true;
+        nx = -1;
+        int most = 0;
+        for (int x = 0; x < nQ; ++x) {
+          const int v = Ux - first_dyn(x) - (int)__builtin_amdgcn_readlane(q_seen, 32 + x);
+          if (v > most) {
+            most = v;
+            nx = x;
+          }
         }
+        if (nx < 0) break;
+        unsigned t = 0;
+        if (lane == 0)
+          t = __hip_atomic_fetch_add(qslot + 16 * nx, 1u, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+        nt = first_dyn(nx) + __builtin_amdgcn_readfirstlane((int)t);
       }
-      if (nx < 0) break;
-      unsigned t = 0;
-      if (lane == 0)
-        t = __hip_atomic_fetch_add(qslot + 16 * nx, 1u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-      nt = first_dyn(nx) + __builtin_amdgcn_readfirstlane((int)t);
+      if (lane == 0) {
+        ua.ux = nx;
+        ua.ut = nt;
+      }
     }
-    if (lane == 0) {
-      ua.ux = nx;
-      ua.ut = nt;
-    }
-  }
-  __syncthreads();
-  if (rfl(ua.ux) < 0) break;
+    __syncthreads();
+    if (rfl(ua.ux) < 0) break;
   }  // units
 
   // The last workgroup to finish returns the slot's counters to zero for the next launch.
