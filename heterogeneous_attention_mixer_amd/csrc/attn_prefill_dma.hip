@@ -112,8 +112,10 @@ __device__ __forceinline__ u32x4 rsrc_words(unsigned long long base, int bytes) 
 // (lds_base wave-uniform, in M0); offsets outside the buffer write zeros. Written as
 // assembly so that the compiler does not see an LDS store: it would otherwise order every
 // later LDS read of the block after these loads and wait for them. Completion is the
-// kernel's business: every tile is read only after an s_waitcnt vmcnt(0) and a barrier that
-// follow its loads, and no compiler-visible vector load is in flight inside the key loop.
+// kernel's business: every tile is read only after an s_waitcnt and a barrier that follow its
+// loads (vmcnt(0) in the pipelined kernel; in the phase-separated one a count that leaves out
+// only the loads of later tiles, which complete in issue order), and no compiler-visible
+// vector load is in flight inside the key loop.
 // `voff` must be a register that is never rewritten while loads are in flight (the
 // per-tile step lives in the descriptor): the address operand of a load inside inline
 // assembly gets no hazard protection from the compiler.
@@ -1028,36 +1030,36 @@ prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ k
                    o[db][r4 * 4 + 1] * inv, o[db][r4 * 4 + 2] * inv, o[db][r4 * 4 + 3] * inv);
       }
     } else {
-    // Differential: out = O1 / l1 - lambda * O2 / l2, map 1's term passed to map 0 through LDS.
-    __syncthreads();  // every wave is done reading the tiles
-    {
-      float* const xch = reinterpret_cast<float*>(smem) + rb * 64 * (DB * 16);
-      if (map == 1) {
-        const float sc = ua.lambda / lsum;
+      // Differential: out = O1 / l1 - lambda * O2 / l2, map 1's term passed to map 0 through LDS.
+      __syncthreads();  // every wave is done reading the tiles
+      {
+        float* const xch = reinterpret_cast<float*>(smem) + rb * 64 * (DB * 16);
+        if (map == 1) {
+          const float sc = ua.lambda / lsum;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) xch[(db * 16 + r) * 64 + lane] = o[db][r] * sc;
+        }
+      }
+      __syncthreads();
+      if (map == 0 && qi < L) {
+        const float inv = 1.0f / lsum;
+        const float* const xch = reinterpret_cast<const float*>(smem) + rb * 64 * (DB * 16);
+        __bf16* orow = rfl_ptr(ua.o) + head + (size_t)qi * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) xch[(db * 16 + r) * 64 + lane] = o[db][r] * sc;
-      }
-    }
-    __syncthreads();
-    if (map == 0 && qi < L) {
-      const float inv = 1.0f / lsum;
-      const float* const xch = reinterpret_cast<const float*>(smem) + rb * 64 * (DB * 16);
-      __bf16* orow = rfl_ptr(ua.o) + head + (size_t)qi * D;
+          for (int r4 = 0; r4 < 4; ++r4) {
+            float x[4];
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          float x[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[e] = o[db][r4 * 4 + e] * inv;
-            x[e] -= xch[(db * 16 + r4 * 4 + e) * 64 + lane];
+            for (int e = 0; e < 4; ++e) {
+              x[e] = o[db][r4 * 4 + e] * inv;
+              x[e] -= xch[(db * 16 + r4 * 4 + e) * 64 + lane];
+            }
+            store4(orow + db * 32 + 8 * r4 + 4 * lg, x[0], x[1], x[2], x[3]);
           }
-          store4(orow + db * 32 + 8 * r4 + 4 * lg, x[0], x[1], x[2], x[3]);
-        }
-    }
+      }
     }
 
     if (rfl(ua.slot) < 0) break;
@@ -1118,8 +1120,6 @@ prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ k
     }
   }
 }
-
-
 
 template <int D, int VAR, int SPL>
 hipError_t launch_dma_s(const PrefillLaunch& a, int nq, hipStream_t stream) {
