@@ -166,7 +166,9 @@ def executed_mfma_split(variant: str, B: int, H: int, L: int, d: int, window: in
     last tile after the loop. With at most one workgroup per CU the key split runs (two
     waves per row block, alternate tiles); otherwise one wave per row block. A wave skips
     the first scores of a tile no row of it sees and the last value product of a tile past
-    its rows, where the kernel does (see the kernel's prologue and tail).
+    its rows, where the kernel does (see the kernel's prologue and tail). Full causal in the
+    key split with an even number of 64-row query tiles pairs tile p with tile n-1-p in one
+    workgroup, and a wave of the light tile ends its loop early (see the kernel's loop).
     Phase-separated kernel, the differential (8 waves: 4 row blocks x 2 maps, 128 rows) and
     full causal on grids of more than one 256-row workgroup per CU (8 waves: 8 row blocks):
     per wave hi + 2 matrix phases of the scores (half-width for the differential) and the
@@ -191,6 +193,24 @@ def executed_mfma_split(variant: str, B: int, H: int, L: int, d: int, window: in
             small += 8 * (hi + 1) * 4
         return B * H * total, B * H * small
     spl = 2 if B * H * nq <= n_cu else 1
+    nt64 = (L + bn - 1) // bn
+    if variant == "full" and spl == 2 and nt64 % 2 == 0:
+        # Paired 64-row query tiles p and nt64-1-p in one workgroup (row blocks 0, 1 and 2, 3),
+        # two waves per row block; a wave's loop ends with the last of its tiles its rows see
+        # (at least one iteration).
+        for p in range(nt64 // 2):
+            th = nt64 - 1 - p
+            n_it = (min(th * bn + bn, L) - 1) // bn // 2 + 1
+            for rb in range(4):
+                qw = p * bn + 32 * rb if rb < 2 else th * bn + 32 * (rb - 2)
+                for half in range(2):
+                    jl = (qw + 31) // bn
+                    n_run = min(n_it, (jl - half) // 2 + 1 if jl >= half else 1)
+                    see_first = half == 0 or half * bn <= qw + 31
+                    tail = (2 * (n_run - 1) + half) * bn <= qw + 31
+                    total += (qk if see_first else 0) + (n_run - 1) * (qk + pv) + pv + \
+                        (pv if tail else 0)
+        return B * H * total, 0
     for qt in range(nq):
         q0 = qt * bm
         hi = (min(q0 + bm, L) - 1) // bn

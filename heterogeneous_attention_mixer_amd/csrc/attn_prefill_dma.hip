@@ -52,6 +52,8 @@
 //     all tiles of a head on one XCD when B*H is a multiple of 8. The phase-separated
 //     kernel launches persistent when it has more units than CUs: one workgroup per CU takes
 //     units from per-XCD queues in that order and steals from the other queues at the end.
+//     Full causal in the key split (at most one workgroup per CU) pairs 64-row query tile t
+//     with its mirror n-1-t in one workgroup, so that every workgroup holds the same work.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -155,7 +157,7 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-template <int D, int VAR, int SPL>
+template <int D, int VAR, int SPL, bool PAIR>
 __global__ void __attribute__((amdgpu_flat_work_group_size(DShape<SPL>::threads,
                                                            DShape<SPL>::threads),
                                amdgpu_waves_per_eu(2, 2)))
@@ -164,6 +166,7 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
                    int G, int nq, int window) {
   static_assert(VAR == kFull || VAR == kSliding, "the differential runs the phase kernel");
   static_assert(SPL == 1 || SPL == 2, "one or two waves per row block");
+  static_assert(!PAIR || (SPL == 2 && VAR == kFull), "paired query tiles: full, key split");
   constexpr bool kSlide = (VAR == kSliding);
   constexpr int kWaves = DShape<SPL>::waves;
   constexpr int kRows = DShape<SPL>::rows;
@@ -191,17 +194,25 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // the same value, in an SGPR
-  const int rb = SPL == 1 ? wave : wave % kRows;       // row block of this wave
-  const int half = SPL == 1 ? 0 : wave / kRows;        // its tile of each iteration
-  const int rb_s = SPL == 1 ? wave_s : wave_s % kRows;  // the same two, in SGPRs
-  const int half_s = SPL == 1 ? 0 : wave_s / kRows;
+  // Row block of this wave and its tile of each iteration. Paired tiles: waves 2r and 2r + 1
+  // split row block r, so that each SIMD (waves w and w + 4) holds a wave of the light tile
+  // and one of the heavy tile.
+  const int rb = SPL == 1 ? wave : (PAIR ? wave >> 1 : wave % kRows);
+  const int half = SPL == 1 ? 0 : (PAIR ? wave & 1 : wave / kRows);
+  const int rb_s = SPL == 1 ? wave_s : (PAIR ? wave_s >> 1 : wave_s % kRows);  // in SGPRs
+  const int half_s = SPL == 1 ? 0 : (PAIR ? wave_s & 1 : wave_s / kRows);
   const int lr = lane & 31;
   const int lg = lane >> 5;
 
   int bh, qt;
   map_unit(blockIdx.x, BH, nq, &bh, &qt, kSlide);
-  const int q0 = qt * BM;
-  const int qw = q0 + rb * 32;
+  // Paired tiles (an even number of 64-row query tiles, nq pairs): row blocks 0 and 1 are the
+  // light tile qt, row blocks 2 and 3 the heavy tile 2 nq - 1 - qt, so that every workgroup
+  // holds the same causal work. q0 is the heavy tile's first row.
+  const int q0 = PAIR ? (2 * nq - 1 - qt) * 64 : qt * BM;
+  auto row0 = [&](int r) { return PAIR ? (r < 2 ? qt * 64 + r * 32 : q0 + (r - 2) * 32)
+                                       : q0 + r * 32; };
+  const int qw = row0(rb);
   const int qi = qw + lr;
   const size_t head = (size_t)bh * (size_t)L * D;         // q and out
   const size_t kv_head = (size_t)(bh / G) * (size_t)L * D;  // k and v: G query heads each
@@ -261,7 +272,7 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   // ---- key tiles the workgroup can see: [lo, hi]. Iteration it takes tiles
   // lo + SPL*it + s (s < SPL), the one at s = half for this wave; with SPL = 2 the second
   // wave's tile of the last iteration may be hi + 1, which no row sees (it is masked).
-  const int q_last = min(q0 + BM, L) - 1;
+  const int q_last = min(q0 + (PAIR ? 64 : BM), L) - 1;
   const int lo = kSlide ? max(0, q0 - window + 1) / BN : 0;
   const int hi = q_last / BN;
   const int n_it = (hi - lo) / SPL + 1;
@@ -425,7 +436,7 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   // the window of the workgroup's first rows, or a second wave's tile past its rows): then
   // zeros stand in, and the mask of the first iteration turns every one of them into -inf.
   const int j0_s = lo + half_s;
-  const int qw_s = q0 + rb_s * 32;  // the wave's first row, as a scalar
+  const int qw_s = row0(rb_s);  // the wave's first row, as a scalar
   const bool see_first = (half_s == 0 || j0_s * BN <= qw_s + 31) &&
                          (!kSlide || j0_s * BN + BN - 1 >= qw_s - window + 1);
   float tmax_n;  // row max of the scores of the next tile (unmasked)
@@ -456,7 +467,7 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
     // buffer PAR (those of iteration it were read during it-1), while it+2 is in the range,
     // and the V tiles of iteration it into V's buffer PAR (those of it-2 were read during
     // it-1).
-    if (!LAST && it + 2 < n_it) load_it(false, kKBuf[PAR], it + 2);
+    if ((PAIR || !LAST) && it + 2 < n_it) load_it(false, kKBuf[PAR], it + 2);
     load_it(true, kVBuf[PAR], it);
     // Rescale decided on the previous tile: O holds the tiles before that one here, and the
     // value product of the previous tile below is already on its reference.
@@ -519,12 +530,17 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   using Odd = std::integral_constant<int, 1>;
   using Inner = std::integral_constant<bool, false>;
   using Last = std::integral_constant<bool, true>;
+  // Paired tiles: a wave's loop ends with the last tile of its own that any of its rows sees
+  // (run as the last iteration: no next scores; its value product follows the loop). Its
+  // remaining iterations only issue its share of the tile loads and meet the barriers.
+  const int jl_w = (qw_s + 31) / BN - lo;  // the wave's last visible tile, from lo
+  const int n_run = PAIR ? min(n_it, jl_w >= half_s ? (jl_w - half_s) / SPL + 1 : 1) : n_it;
   int it = 0;
-  for (; it + 2 < n_it; it += 2) {  // it even; it and it + 1 both before the last
+  for (; it + 2 < n_run; it += 2) {  // it even; it and it + 1 both before the last
     iter(Even{}, Inner{}, it);
     iter(Odd{}, Inner{}, it + 1);
   }
-  if (it + 1 < n_it) iter(Even{}, Inner{}, it++);  // it was n_it - 2
+  if (it + 1 < n_run) iter(Even{}, Inner{}, it++);  // it was n_run - 2
   if (it & 1)
     iter(Odd{}, Last{}, it);
   else
@@ -540,6 +556,18 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
     else
       pv(std::integral_constant<int, kVImm[0]>{}, pr[0]);
   }
+  // Paired tiles: a wave whose loop ended early meets the remaining iterations' barriers with
+  // its share of their tile loads. Its last value product above read the V tile of its last
+  // iteration, which the loads of the iteration two later (after the next barrier) replace.
+  if constexpr (PAIR) {
+    for (int t = it + 1; t < n_it; ++t) {
+      const int par = t & 1;
+      if (t + 2 < n_it) load_it(false, par ? kKBuf[1] : kKBuf[0], t + 2);
+      load_it(true, par ? kVBuf[1] : kVBuf[0], t);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+    }
+  }
 
   // ---- epilogue: out = O / l. Element (db, r) of a lane is channel
   // db*32 + 8*(r/4) + 4*lg + r%4 of query qi. The lane's indices are taken afresh here (the
@@ -547,7 +575,7 @@ prefill_dma_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ kg,
   // live through the key loop for it.
   const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int lg_e = lane_e >> 5;
-  const int qi_e = q0 + rb_s * 32 + (lane_e & 31);
+  const int qi_e = row0(rb_s) + (lane_e & 31);
   float lsum = xhalf_sum(l);
   if constexpr (SPL == 2) {
     // The second wave of each row block hands its state (reference m, row sum, O) to the
@@ -1121,10 +1149,10 @@ prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ k
   }
 }
 
-template <int D, int VAR, int SPL>
+template <int D, int VAR, int SPL, bool PAIR = false>
 hipError_t launch_dma_s(const PrefillLaunch& a, int nq, hipStream_t stream) {
   const int BH = a.B * a.H;
-  hipLaunchKernelGGL((prefill_dma_kernel<D, VAR, SPL>), dim3((unsigned)(BH * nq)),
+  hipLaunchKernelGGL((prefill_dma_kernel<D, VAR, SPL, PAIR>), dim3((unsigned)(BH * nq)),
                      dim3(DShape<SPL>::threads), 0, stream, static_cast<const __bf16*>(a.q),
                      static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
                      static_cast<__bf16*>(a.out), a.L, BH, a.H / a.Hkv, nq, a.window);
@@ -1133,7 +1161,9 @@ hipError_t launch_dma_s(const PrefillLaunch& a, int nq, hipStream_t stream) {
 
 // Full and sliding: the key split (SPL = 2) when the grid holds at most one workgroup per
 // CU, where the 4-wave workgroups would leave one wave per SIMD and the longest query tile
-// alone would set the time; otherwise two 4-wave workgroups per CU.
+// alone would set the time; otherwise two 4-wave workgroups per CU. Full causal with an even
+// number of 64-row query tiles pairs them in the key split, light with heavy, so that every
+// workgroup holds the same work and the heaviest no longer sets the time alone.
 template <int D, int VAR>
 hipError_t launch_dma_t(const PrefillLaunch& a, hipStream_t stream) {
   constexpr int BM = DShape<1>::bm;
@@ -1144,8 +1174,11 @@ hipError_t launch_dma_t(const PrefillLaunch& a, hipStream_t stream) {
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  return wgs <= cus ? launch_dma_s<D, VAR, 2>(a, nq, stream)
-                    : launch_dma_s<D, VAR, 1>(a, nq, stream);
+  if (wgs > cus) return launch_dma_s<D, VAR, 1>(a, nq, stream);
+  const int nt64 = (a.L + 63) / 64;
+  if (VAR == kFull && (nt64 & 1) == 0)
+    return launch_dma_s<D, kFull, 2, true>(a, nt64 / 2, stream);
+  return launch_dma_s<D, VAR, 2>(a, nq, stream);
 }
 
 // The queue slot of (device, stream): the stream's rank among the streams of that device

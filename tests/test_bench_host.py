@@ -78,6 +78,39 @@ def test_executed_mfmas_closed_forms():
         bench.executed_mfmas("sliding", 1, 1, 1920, 128, 1024, n_cu=0) == full_tiles
 
 
+def _paired_mfmas_by_simulation(B, H, L, d):
+    # The paired key-split loop of the full kernel, wave by wave and iteration by iteration:
+    # the prologue's scores, then per iteration the value product of the tile two back and,
+    # unless the iteration is the wave's last, the scores of the tile two ahead; a wave's
+    # iterations are those of its tiles its rows see (at least its first); the value product
+    # of its last tile after the loop if its rows see that tile.
+    qk, pv = 2 * (d // 16), 4 * (d // 32)
+    nt = (L + 63) // 64
+    total = 0
+    for p in range(nt // 2):
+        th = nt - 1 - p
+        n_it = (min(th * 64 + 64, L) - 1) // 64 // 2 + 1
+        for rb in range(4):
+            first = p * 64 + 32 * rb if rb < 2 else th * 64 + 32 * (rb - 2)
+            last_tile = (first + 31) // 64
+            for half in range(2):
+                its = [it for it in range(n_it) if 2 * it + half <= last_tile] or [0]
+                n = qk if (half == 0 or 64 * half <= first + 31) else 0
+                for it in its:
+                    n += pv + (qk if it != its[-1] else 0)
+                if (2 * its[-1] + half) * 64 <= first + 31:
+                    n += pv
+                total += n
+    return B * H * total
+
+
+@pytest.mark.parametrize("B,H,L,d", [(1, 16, 2048, 128), (1, 3, 128, 128), (2, 3, 1000, 64),
+                                     (1, 1, 1989, 128), (1, 16, 640, 64)])
+def test_executed_mfmas_of_paired_tiles(B, H, L, d):
+    assert B * H * ((L + 127) // 128) <= 256 and ((L + 63) // 64) % 2 == 0
+    assert bench.executed_mfmas("full", B, H, L, d, 0) == _paired_mfmas_by_simulation(B, H, L, d)
+
+
 @pytest.mark.parametrize("variant,L,W", [("full", 1, 0), ("full", 300, 0), ("full", 2048, 0),
                                          ("sliding", 777, 100), ("sliding", 8192, 1024),
                                          ("differential", 129, 0), ("differential", 4096, 0)])
@@ -100,6 +133,26 @@ def test_executed_mfmas_match_the_committed_counters():
             pytest.skip("no SQ summary for the current kernel source")
         w = 1024 if v == "sliding" else 0
         assert sq["sq_insts_mfma"] == bench.executed_mfmas(v, 1, 16, 8192, 128, w)
+
+
+def test_executed_mfmas_match_the_counters_at_every_bench_length():
+    # SQ_INSTS_MFMA of one profiled run over the stack and the sweep points (full at 2K, 8K
+    # and 32K, including the paired key split at 2K; the differential at 8K and 32K; sliding
+    # at 8K), committed with the kernel source hash it was taken on.
+    path = os.path.join(ROOT, "profiles", "mfma_counts_by_length.txt")
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != bench.kernel_source_hash():
+        pytest.skip("the counts were taken on another kernel source")
+    for variant, L in (("full", 2048), ("full", 8192), ("full", 32768), ("sliding", 8192),
+                       ("differential", 8192), ("differential", 32768)):
+        w = 1024 if variant == "sliding" else 0
+        assert int(kv[f"{variant}_L{L}_sq_insts_mfma"]) == \
+            bench.executed_mfmas(variant, 1, 16, L, 128, w), (variant, L)
 
 
 def test_write_sq_reads_busy_share_and_clock(tmp_path, monkeypatch):
