@@ -764,7 +764,8 @@ prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ k
   }
 
   // Units: (batch x head, query tile) pairs. With B*H a multiple of 8 there is one queue
-  // per XCD, holding that XCD's heads heaviest tile first (the order map_unit deals them);
+  // per XCD, holding that XCD's heads heaviest tile first (full: the heads interleaved, as
+  // map_unit deals them; the differential: head by head, as map_unit_head_major does);
   // otherwise one queue. Workgroup b starts on ticket b / nQ of queue b % nQ (its XCD's, as
   // the hardware deals workgroups to the XCDs round-robin). With a slot (the persistent
   // launch, one workgroup per CU), it then takes the next ticket of that queue, and once
@@ -784,7 +785,13 @@ prefill_phase_kernel(const __bf16* __restrict__ qg, const __bf16* __restrict__ k
     {
       const int BHu = rfl(ua.BH), nqu = rfl(ua.nq);
       const int nQ = ((BHu & 7) == 0) ? kQueues : 1;
-      map_unit(rfl(ua.ut) * nQ + rfl(ua.ux), BHu, nqu, &bh, &qt);
+      // The differential's queues hold their units head by head (its HBM traffic falls by
+      // about 40 % and its time does not move); full keeps the heads interleaved, which is
+      // faster for it.
+      if constexpr (kDiff)
+        map_unit_head_major(rfl(ua.ut) * nQ + rfl(ua.ux), BHu, nqu, &bh, &qt);
+      else
+        map_unit(rfl(ua.ut) * nQ + rfl(ua.ux), BHu, nqu, &bh, &qt);
     }
     const int q0 = qt * BM;
     const int qw = q0 + rb * 32;

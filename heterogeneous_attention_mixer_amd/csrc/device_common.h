@@ -123,4 +123,23 @@ __device__ __forceinline__ void map_unit(int bid, int BH, int nq, int* bh, int* 
   *qt = ascending ? rank : nq - 1 - rank;
 }
 
+// The same units, head by head: an XCD's (or, when the head count is not a multiple of 8,
+// the grid's) heads one after another, each heaviest query tile first. Taken from a work
+// queue in this order, the units in flight at once mostly belong to one head, whose K/V
+// (4 MiB at L=8192, d=128) fits one L2, so fewer K/V tiles are fetched from HBM again.
+__device__ __forceinline__ void map_unit_head_major(int bid, int BH, int nq, int* bh,
+                                                    int* qt) {
+  int head, rank;
+  if ((BH & 7) == 0) {
+    const int x = bid & 7, j = bid >> 3, hpx = BH >> 3;
+    head = x * hpx + j / nq;
+    rank = j % nq;
+  } else {
+    head = bid / nq;
+    rank = bid % nq;
+  }
+  *bh = head;
+  *qt = nq - 1 - rank;
+}
+
 }  // namespace mixer
